@@ -1,0 +1,171 @@
+/*
+ * hbl.h — C ABI of the H-BitLinear forward pass on AMD Instinct MI355X (gfx950).
+ *
+ * The layer (BitNet v2, "H-BitLinear" as described on the arXiv abstract page of
+ * "BitNet v2: Native 4-bit Activations with Hadamard Transformation for 1-bit LLMs"
+ * and in the section "H-BitLinear模塊" of the Traditional-Chinese write-up of that
+ * paper) replaces the bias-free nn.Linear of the attention output projection Wo and
+ * the FFN down projection Wdown.  For one token row x (length K) it computes
+ *
+ *     u  = RMSNorm(x)                      (optional; unit or given gamma)
+ *     z  = H_K u                           (online fast Walsh-Hadamard transform)
+ *     q  = absmax_quant(z) in INT4 or INT8 (per token, no zero point)
+ *     y  = (q . t^T) * scales              (t = per-tensor absmean ternary weights)
+ *
+ * and the same without H for a plain BitLinear (all other linears of the model).
+ *
+ * Numerics (the pages drop every equation; the readings below are the contract, and
+ * the test oracle implements exactly these steps on the CPU):
+ *
+ *  Weights (write-up, section H-BitLinear模塊: per-tensor absmean ternarisation;
+ *  bitnet.cpp article, section "6 页论文，引入 1 bit LLM": scale by the mean absolute
+ *  value, then round to the nearest of -1, 0, 1):
+ *      S      = sum over rows n ascending of (sum over k ascending of |W[n,k]|), in fp64
+ *      alpha  = max( (float)(S / (N*K)), 1e-5f )
+ *      t[n,k] = clamp( rint_ne( fl32(W[n,k] / alpha) ), -1, 1 )
+ *
+ *  Activations, per row m (write-up, section H-BitLinear模塊: LN, then Hadamard by FHT,
+ *  then INT8/INT4 quantisation; bitnet.cpp article: activations scaled into [-Qb, Qb]
+ *  with no zero point).  Qb = 7 (abits 4) or 127 (abits 8):
+ *      xf   = (float) x                                  (bf16 -> fp32 is exact)
+ *      u_k  = norm ? fl32(xf_k * gamma_k) : xf_k           (gamma == NULL means gamma = 1)
+ *      r    = norm ? (float)(1 / sqrt( (sum_k xf_k^2 in fp64, k ascending)/K + eps )) : 1
+ *      z    = use_hadamard ? FWHT_fp32(u) : u             (butterfly stages h = 1,2,4,..,K/2,
+ *                                                          each pair (j, j+h) -> (a+b, a-b) in fp32;
+ *                                                          z = H_K u with H_K[i][j] = (-1)^popcount(i&j))
+ *      g    = max_k |z_k|
+ *      if g == 0:  q = 0 and deq = 0
+ *      else:       s = fl32(Qb / g);  q_k = clamp( rint_ne( fl32(z_k * s) ), -Qb-1, Qb )
+ *                  deq = fl32( fl32( fl32(g / Qb) * r ) * hK ),  hK = use_hadamard ? (float)(1/sqrt(K)) : 1
+ *  The Hadamard transform is the orthonormal one, H_K / sqrt(K); the 1/sqrt(K) and the
+ *  RMSNorm factor r are folded into deq (absmax codes are invariant under any positive
+ *  per-row scale, so the codes do not depend on them).
+ *
+ *  GEMM and epilogue:
+ *      acc[m,n] = sum_k q[m,k] * t[n,k]          (exact, int32)
+ *      y[m,n]   = fl32( fl32( (float)acc[m,n] * deq[m] ) * alpha )
+ *
+ * Packed formats (not given by the pages; chosen so the GEMM can widen them to int8
+ * MFMA operands with two or three bit operations per 32-bit word):
+ *
+ *  Wq — packed ternary weights, N rows of K/4 bytes, row-major.  Row n is a sequence of
+ *       little-endian 32-bit words; word w holds the 16 weights k = 16w + c, c = 0..15.
+ *       Weight c sits in the 2-bit field p = 4*(c % 4) + c/4 (bits 2p and 2p+1), encoded
+ *       as 2-bit two's complement: 0b00 = 0, 0b01 = +1, 0b11 = -1 (0b10 never appears).
+ *
+ *  codes, abits = 8 — int8 two's complement, M rows of K bytes, natural order.
+ *
+ *  codes, abits = 4 — M rows of K/2 bytes.  Each 8-byte group G of a row holds the codes
+ *       k = 16G + c, c = 0..15.  Byte j (0..7) of the group holds, as 4-bit two's
+ *       complement nibbles, code c0 = (j % 4) + 8*(j / 4) in its low nibble and code c0+4
+ *       in its high nibble.
+ *
+ *  deq — one fp32 per row.
+ *
+ * Conventions for every entry point:
+ *  - Every pointer argument is a device pointer (hipMalloc / torch CUDA memory) unless
+ *    stated otherwise, 16-byte aligned.  The caller owns every buffer; the library never
+ *    allocates device memory and keeps no mutable global state.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All work is
+ *    enqueued asynchronously on that stream.  Calls on different streams are independent.
+ *  - Arguments are validated synchronously, before any HIP call.  An invalid argument
+ *    returns a status other than HBL_OK, enqueues nothing, and sets a per-thread message
+ *    readable with hbl_last_error().  A kernel launch error returns HBL_ERR_HIP.  Faults
+ *    inside kernels surface at the caller's next synchronisation of the stream.
+ *  - Sizes are int64_t.  M == 0 is a valid no-op for every call that takes M.
+ *  - Inputs with NaN or infinities give unspecified codes and outputs.
+ *  - No C++ exception crosses this interface.
+ */
+#ifndef HBL_H_
+#define HBL_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HBL_OK = 0,
+  HBL_ERR_INVALID_ARG = 1, /* null pointer, negative size, abits not 4/8, misaligned ... */
+  HBL_ERR_UNSUPPORTED = 2, /* a valid request outside what the kernels implement       */
+  HBL_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the *_workspace_bytes  */
+  HBL_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed               */
+} hbl_status;
+
+typedef enum { HBL_F32 = 0, HBL_BF16 = 1 } hbl_dtype;
+typedef enum { HBL_NORM_NONE = 0, HBL_NORM_RMS = 1 } hbl_norm;
+
+/* Limits of this implementation.
+ *  K % 64 == 0 and 64 <= K <= HBL_MAX_K for every call.
+ *  With use_hadamard, K is also a power of two and K <= HBL_MAX_K_HADAMARD
+ *  (the transform keeps one fp32 row on chip).
+ *  |acc| <= 127*K < 2^24 for K <= HBL_MAX_K, so (float)acc is exact. */
+#define HBL_MAX_K 131072
+#define HBL_MAX_K_HADAMARD 32768
+
+/* Byte sizes of the packed buffers (0 for invalid arguments). */
+size_t hbl_packed_weight_bytes(int64_t N, int64_t K);           /* N*K/4          */
+size_t hbl_packed_act_bytes(int64_t M, int64_t K, int abits);   /* M*K*abits/8    */
+/* Workspace of hbl_quantize_weights: N fp64 row sums.  */
+size_t hbl_wquant_workspace_bytes(int64_t N, int64_t K);
+/* Workspace of hbl_forward: the codes and deq of M rows (256-byte aligned pieces). */
+size_t hbl_forward_workspace_bytes(int64_t M, int64_t K, int abits);
+
+/* hbl_quantize_weights — per-tensor absmean ternarisation and 2-bit packing.
+ * (write-up section H-BitLinear模塊; bitnet.cpp article section "6 页论文，引入 1 bit LLM")
+ *  W        [N, K] fp32, row-major (out x in, the nn.Linear convention).
+ *  Wq       [N, K/4] bytes, written in the Wq format above.
+ *  w_scale  one fp32 on the device: alpha.
+ *  ws       workspace of at least hbl_wquant_workspace_bytes(N, K) bytes.
+ *  N >= 1.  Deterministic: alpha is computed in the fixed order stated above. */
+hbl_status hbl_quantize_weights(const float* W, int64_t N, int64_t K, uint8_t* Wq, float* w_scale,
+                                void* ws, size_t ws_bytes, void* stream);
+
+/* hbl_quantize_activations — load, optional RMSNorm, optional online FWHT, per-token
+ * absmax quantisation and packing (write-up section H-BitLinear模塊).
+ *  x        [M, K] of dtype xt, row-major.
+ *  gamma    [K] fp32 RMSNorm weight, or NULL for unit gamma; ignored if norm == NONE.
+ *  norm_eps RMSNorm epsilon (finite, >= 0).
+ *  codes    [M, K*abits/8] bytes in the codes format above.
+ *  deq      [M] fp32 per-row dequantisation factor. */
+hbl_status hbl_quantize_activations(const void* x, hbl_dtype xt, int64_t M, int64_t K, hbl_norm norm,
+                                    const float* gamma, float norm_eps, int abits, int use_hadamard,
+                                    uint8_t* codes, float* deq, void* stream);
+
+/* hbl_gemm_s32 — the integer product acc = q . t^T (exact), for inspection and tests.
+ *  codes [M, K*abits/8], Wq [N, K/4], acc [M, N] int32 row-major.  N >= 1. */
+hbl_status hbl_gemm_s32(const uint8_t* codes, const uint8_t* Wq, int64_t M, int64_t K, int64_t N,
+                        int abits, int32_t* acc, void* stream);
+
+/* hbl_gemm_dequant — integer product plus the dequantisation epilogue
+ *  y[m,n] = fl32(fl32((float)acc[m,n] * deq[m]) * (*w_scale)), y [M, N] fp32 row-major. */
+hbl_status hbl_gemm_dequant(const uint8_t* codes, const float* deq, const uint8_t* Wq,
+                            const float* w_scale, int64_t M, int64_t K, int64_t N, int abits, float* y,
+                            void* stream);
+
+/* hbl_forward — the whole H-BitLinear (use_hadamard = 1) or BitLinear (use_hadamard = 0)
+ * forward: hbl_quantize_activations into the workspace, then hbl_gemm_dequant into y.
+ *  ws  at least hbl_forward_workspace_bytes(M, K, abits) bytes of device memory. */
+hbl_status hbl_forward(const void* x, hbl_dtype xt, const uint8_t* Wq, const float* w_scale, int64_t M,
+                       int64_t K, int64_t N, int abits, int use_hadamard, hbl_norm norm,
+                       const float* gamma, float norm_eps, float* y, void* ws, size_t ws_bytes,
+                       void* stream);
+
+/* hbl_swiglu — the FFN gate of the LLaMA-like block (write-up section
+ * "BitNet v2：原生4位激活": RMSNorm, SwishGLU, no bias):
+ *  h[i] = fl32( silu(g[i]) * u[i] ),  silu(v) = v / (1 + exp(-v)) in fp32.
+ *  g, u, h: n fp32 each; h may alias neither g nor u.  n >= 0. */
+hbl_status hbl_swiglu(const float* g, const float* u, int64_t n, float* h, void* stream);
+
+/* Static text for a status code, and the detail of the last failure on this thread. */
+const char* hbl_status_string(hbl_status s);
+const char* hbl_last_error(void);
+/* Library version: major*10000 + minor*100 + patch. */
+int hbl_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HBL_H_ */

@@ -1,0 +1,254 @@
+"""ctypes front end of the C oracle (hbl_oracle.c).  Test infrastructure only.
+
+Every function takes and returns numpy arrays.  Activations are either float32 arrays or
+bf16 bit patterns held in uint16 arrays (``dtype`` = BF16).  Nothing here does any of the
+method's arithmetic except :func:`dense_reference`, the fp64 "unquantised" reference used
+to bound quantisation error (it follows the same pages: RMSNorm, then the orthonormal
+Hadamard transform, then the product with the dequantised ternary weights).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+F32 = 0
+BF16 = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "hbl_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+
+def lib_path() -> str:
+    return _LIB
+
+
+def build(force: bool = False) -> str:
+    """Compile hbl_oracle.c with gcc (plain C11, OpenMP, no FMA contraction, no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + f".tmp{os.getpid()}"
+        cmd = ["gcc", "-std=c11", "-O2", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+               "-fno-fast-math", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        I = ctypes.c_int
+        Fl = ctypes.c_float
+        lib.orc_num_threads.restype = I
+        lib.orc_set_num_threads.argtypes = [I]
+        lib.orc_fwht_f32.argtypes = [P, I64]
+        lib.orc_fwht_f64.argtypes = [P, I64]
+        lib.orc_quantize_weights.argtypes = [P, I64, I64, P, P]
+        lib.orc_quantize_weights.restype = I
+        lib.orc_quantize_activations.argtypes = [P, I, I64, I64, I, P, Fl, I, I, P, P, P]
+        lib.orc_quantize_activations.restype = I
+        lib.orc_gemm_s32.argtypes = [P, P, I64, I64, I64, P]
+        lib.orc_gemm_s32.restype = I
+        lib.orc_dequant.argtypes = [P, P, Fl, I64, I64, P]
+        lib.orc_dequant.restype = I
+        lib.orc_forward.argtypes = [P, I, P, Fl, I64, I64, I64, I, I, I, P, Fl, P, P, P, P]
+        lib.orc_forward.restype = I
+        lib.orc_swiglu.argtypes = [P, P, I64, P]
+        lib.orc_pack_weights.argtypes = [P, I64, I64, P]
+        lib.orc_pack_weights.restype = I
+        lib.orc_unpack_weights.argtypes = [P, I64, I64, P]
+        lib.orc_unpack_weights.restype = I
+        lib.orc_pack_codes.argtypes = [P, I64, I64, I, P]
+        lib.orc_pack_codes.restype = I
+        lib.orc_unpack_codes.argtypes = [P, I64, I64, I, P]
+        lib.orc_unpack_codes.restype = I
+        _lib = lib
+        return lib
+
+
+def _p(a: np.ndarray | None):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def num_threads() -> int:
+    return int(_load().orc_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    _load().orc_set_num_threads(int(n))
+
+
+def _xdtype(x: np.ndarray) -> int:
+    if x.dtype == np.float32:
+        return F32
+    if x.dtype == np.uint16:
+        return BF16
+    raise TypeError("activations must be float32 or uint16 (bf16 bit patterns)")
+
+
+def fwht_f32(v) -> np.ndarray:
+    """Unnormalised Sylvester-order FWHT in fp32, ascending butterfly stages (copy)."""
+    out = _c(v, np.float32).copy()
+    n = out.shape[-1]
+    rows = out.reshape(-1, n)
+    for r in rows:
+        _load().orc_fwht_f32(_p(r), n)
+    return out
+
+
+def fwht_f64(v) -> np.ndarray:
+    out = _c(v, np.float64).copy()
+    n = out.shape[-1]
+    rows = out.reshape(-1, n)
+    for r in rows:
+        _load().orc_fwht_f64(_p(r), n)
+    return out
+
+
+def quantize_weights(W) -> tuple[np.ndarray, float]:
+    """Per-tensor absmean ternarisation: returns (t int8 [N,K], alpha)."""
+    W = _c(W, np.float32)
+    N, K = W.shape
+    T = np.empty((N, K), np.int8)
+    a = np.zeros(1, np.float32)
+    if _load().orc_quantize_weights(_p(W), N, K, _p(T), _p(a)) != 0:
+        raise ValueError("orc_quantize_weights: bad arguments")
+    return T, float(a[0])
+
+
+def quantize_activations(x, abits: int, use_h: bool, norm: bool = False, gamma=None, eps: float = 1e-5):
+    """Returns (q int8 [M,K] unpacked, deq f32 [M], r f32 [M])."""
+    x = np.ascontiguousarray(x)
+    M, K = x.shape
+    q = np.empty((M, K), np.int8)
+    deq = np.empty(M, np.float32)
+    r = np.empty(M, np.float32)
+    g = None if gamma is None else _c(gamma, np.float32)
+    rc = _load().orc_quantize_activations(_p(x), _xdtype(x), M, K, int(bool(norm)), _p(g), float(eps),
+                                          int(abits), int(bool(use_h)), _p(q), _p(deq), _p(r))
+    if rc != 0:
+        raise ValueError("orc_quantize_activations: bad arguments")
+    return q, deq, r
+
+
+def gemm_s32(q, T) -> np.ndarray:
+    q = _c(q, np.int8)
+    T = _c(T, np.int8)
+    M, K = q.shape
+    N, K2 = T.shape
+    assert K == K2
+    acc = np.empty((M, N), np.int32)
+    if _load().orc_gemm_s32(_p(q), _p(T), M, K, N, _p(acc)) != 0:
+        raise ValueError("orc_gemm_s32: bad arguments")
+    return acc
+
+
+def dequant(acc, deq, alpha: float) -> np.ndarray:
+    acc = _c(acc, np.int32)
+    deq = _c(deq, np.float32)
+    M, N = acc.shape
+    y = np.empty((M, N), np.float32)
+    _load().orc_dequant(_p(acc), _p(deq), float(alpha), M, N, _p(y))
+    return y
+
+
+def forward(x, T, alpha: float, abits: int, use_h: bool, norm: bool = False, gamma=None, eps: float = 1e-5,
+            intermediates: bool = False):
+    """Whole forward on the rows of x.  Returns y, or (y, q, acc, deq) with intermediates."""
+    x = np.ascontiguousarray(x)
+    T = _c(T, np.int8)
+    M, K = x.shape
+    N = T.shape[0]
+    y = np.empty((M, N), np.float32)
+    q = np.empty((M, K), np.int8) if intermediates else None
+    acc = np.empty((M, N), np.int32) if intermediates else None
+    deq = np.empty(M, np.float32) if intermediates else None
+    g = None if gamma is None else _c(gamma, np.float32)
+    rc = _load().orc_forward(_p(x), _xdtype(x), _p(T), float(alpha), M, K, N, int(abits), int(bool(use_h)),
+                             int(bool(norm)), _p(g), float(eps), _p(y), _p(q), _p(acc), _p(deq))
+    if rc != 0:
+        raise ValueError("orc_forward: bad arguments")
+    return (y, q, acc, deq) if intermediates else y
+
+
+def swiglu(g, u) -> np.ndarray:
+    g = _c(g, np.float32)
+    u = _c(u, np.float32)
+    assert g.shape == u.shape
+    h = np.empty_like(g)
+    _load().orc_swiglu(_p(g), _p(u), g.size, _p(h))
+    return h
+
+
+def pack_weights(T) -> np.ndarray:
+    T = _c(T, np.int8)
+    N, K = T.shape
+    Wq = np.empty((N, K // 4), np.uint8)
+    if _load().orc_pack_weights(_p(T), N, K, _p(Wq)) != 0:
+        raise ValueError("orc_pack_weights: bad arguments")
+    return Wq
+
+
+def unpack_weights(Wq, K: int) -> np.ndarray:
+    Wq = _c(Wq, np.uint8)
+    N = Wq.shape[0]
+    T = np.empty((N, K), np.int8)
+    if _load().orc_unpack_weights(_p(Wq), N, K, _p(T)) != 0:
+        raise ValueError("orc_unpack_weights: bad arguments")
+    return T
+
+
+def pack_codes(q, abits: int) -> np.ndarray:
+    q = _c(q, np.int8)
+    M, K = q.shape
+    out = np.empty((M, K * abits // 8), np.uint8)
+    if _load().orc_pack_codes(_p(q), M, K, int(abits), _p(out)) != 0:
+        raise ValueError("orc_pack_codes: bad arguments")
+    return out
+
+
+def unpack_codes(codes, K: int, abits: int) -> np.ndarray:
+    codes = _c(codes, np.uint8)
+    M = codes.shape[0]
+    q = np.empty((M, K), np.int8)
+    if _load().orc_unpack_codes(_p(codes), M, K, int(abits), _p(q)) != 0:
+        raise ValueError("orc_unpack_codes: bad arguments")
+    return q
+
+
+def dense_reference(x, T, alpha: float, use_h: bool, norm: bool = False, gamma=None, eps: float = 1e-5):
+    """fp64 layer output without activation quantisation: y* = (H_K/sqrt(K)) RMSNorm(x) . (alpha t)^T.
+
+    It is what the quantised forward approximates; tests use it to bound the error of the
+    INT4 / INT8 paths.
+    """
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.uint16:
+        xf = (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    else:
+        xf = x.astype(np.float64)
+    K = xf.shape[1]
+    u = xf
+    if norm:
+        r = 1.0 / np.sqrt((xf * xf).sum(axis=1, keepdims=True) / K + eps)
+        u = xf * (1.0 if gamma is None else np.asarray(gamma, np.float64)) * r
+    if use_h:
+        u = fwht_f64(u) / np.sqrt(K)
+    return u @ (alpha * np.asarray(T, np.float64)).T

@@ -1,0 +1,131 @@
+"""Pins of the oracle's weight ternariser and activation quantiser.
+
+Pages: per-tensor absmean ternary weights (BitNet v2 write-up, section H-BitLinear模塊;
+bitnet.cpp article, section "6 页论文，引入 1 bit LLM": scale by the mean absolute value,
+round to the nearest of -1, 0, 1); activations scaled into [-Qb, Qb] without a zero point,
+per token, INT8 or INT4 (same sections).  The checks use hand-computed fixtures, the
+statistics of the rule on Gaussian weights, and invariants that any correct absmax
+quantiser has.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+@pytest.mark.parametrize("case", _load("ternary_small.json")["cases"], ids=lambda c: c["note"][:30])
+def test_ternary_fixture(orc, case):
+    T, alpha = orc.quantize_weights(np.array(case["W"], np.float32))
+    assert alpha == np.float32(case["alpha"])
+    np.testing.assert_array_equal(T, np.array(case["t"], np.int8))
+
+
+def test_ternary_zero_fraction_on_gaussian(orc):
+    # For W ~ N(0, s^2): alpha -> s*sqrt(2/pi); t = 0 iff |W| < alpha/2, probability
+    # 2*Phi(sqrt(2/pi)/2) - 1 = 0.3101...
+    W = (np.random.default_rng(1).standard_normal((1024, 4096)) * 0.02).astype(np.float32)
+    T, alpha = orc.quantize_weights(W)
+    assert abs(alpha - 0.02 * math.sqrt(2 / math.pi)) < 2e-5
+    p0 = math.erf(math.sqrt(2 / math.pi) / 2 / math.sqrt(2))
+    frac0 = float((T == 0).mean())
+    assert abs(frac0 - p0) < 2e-3
+    assert abs(float((T == 1).mean()) - float((T == -1).mean())) < 2e-3
+
+
+def test_ternary_alpha_matches_fp64_mean(orc):
+    W = (np.random.default_rng(2).standard_normal((300, 640)) * 0.02).astype(np.float32)
+    _, alpha = orc.quantize_weights(W)
+    assert alpha == np.float32(np.abs(W.astype(np.float64)).mean())
+
+
+def test_ternary_is_scale_invariant(orc):
+    W = (np.random.default_rng(4).standard_normal((64, 256)) * 0.02).astype(np.float32)
+    T1, a1 = orc.quantize_weights(W)
+    T2, a2 = orc.quantize_weights(W * np.float32(8.0))
+    np.testing.assert_array_equal(T1, T2)
+    assert a2 == a1 * 8
+
+
+@pytest.mark.parametrize("case", _load("act_quant_small.json")["cases"], ids=lambda c: c["note"][:30])
+def test_act_quant_fixture(orc, case):
+    x = np.array([case["x"]], np.float32)
+    q, deq, r = orc.quantize_activations(x, case["abits"], use_h=False)
+    np.testing.assert_array_equal(q[0], np.array(case["q"], np.int8))
+    assert deq[0] == np.float32(case["deq"])
+    assert r[0] == 1.0
+
+
+@pytest.mark.parametrize("abits,Qb", [(4, 7), (8, 127)])
+@pytest.mark.parametrize("use_h", [False, True])
+def test_act_quant_invariants(orc, abits, Qb, use_h):
+    rng = np.random.default_rng(abits + 10 * use_h)
+    M, K = 64, 1024
+    x = (rng.standard_normal((M, K)) * rng.uniform(0.01, 100, size=(M, 1))).astype(np.float32)
+    q, deq, _ = orc.quantize_activations(x, abits, use_h=use_h)
+    # codes stay in [-Qb, Qb]; the max-magnitude entry maps to +-Qb exactly
+    assert q.min() >= -Qb and q.max() <= Qb
+    assert (np.abs(q).max(axis=1) == Qb).all()
+    # invariance under power-of-two scaling of a row
+    q2, deq2, _ = orc.quantize_activations(x * np.float32(0.25), abits, use_h=use_h)
+    np.testing.assert_array_equal(q, q2)
+    np.testing.assert_array_equal(deq2, deq * np.float32(0.25))
+    # error bound: |z/sqrt(K)^h - q*deq| <= deq/2 (+ rounding of s and deq), z from fp64 FWHT
+    z = orc.fwht_f64(x.astype(np.float64)) / math.sqrt(K) if use_h else x.astype(np.float64)
+    err = np.abs(z - q.astype(np.float64) * deq[:, None].astype(np.float64))
+    assert (err <= deq[:, None] * (0.5 + 1e-3)).all()
+
+
+def test_act_quant_rmsnorm_scale(orc):
+    rng = np.random.default_rng(9)
+    M, K = 16, 512
+    x = rng.standard_normal((M, K)).astype(np.float32) * 3
+    eps = 1e-5
+    _, _, r = orc.quantize_activations(x, 4, use_h=True, norm=True, eps=eps)
+    want = 1.0 / np.sqrt(np.mean(x.astype(np.float64) ** 2, axis=1) + eps)
+    np.testing.assert_allclose(r, want, rtol=2 ** -23)
+    # norm only rescales deq; the codes are those of the un-normalised row (unit gamma)
+    q0, deq0, _ = orc.quantize_activations(x, 4, use_h=True, norm=False)
+    q1, deq1, _ = orc.quantize_activations(x, 4, use_h=True, norm=True, eps=eps)
+    np.testing.assert_array_equal(q0, q1)
+    np.testing.assert_allclose(deq1, deq0 * r, rtol=2 ** -22)
+
+
+def test_act_quant_gamma_applies_per_channel(orc):
+    rng = np.random.default_rng(12)
+    M, K = 8, 256
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    gamma = rng.uniform(0.5, 2.0, K).astype(np.float32)
+    qg, deqg, rg = orc.quantize_activations(x, 8, use_h=True, norm=True, gamma=gamma)
+    qx, deqx, _ = orc.quantize_activations(x * gamma, 8, use_h=True, norm=False)
+    np.testing.assert_array_equal(qg, qx)
+    np.testing.assert_allclose(deqg, deqx * rg, rtol=2 ** -22)
+
+
+def test_fold_matches_textbook_order(orc):
+    """Normalise, transform, then quantise (textbook order) gives the same codes as folding
+    the RMS factor and 1/sqrt(K) into deq, up to rounding-boundary cases."""
+    from bit_quantized_gemm_bitlinear_amd import inputs
+
+    M, K = 256, 2048
+    x = inputs.make_activations("mixture", M, K, outlier_frac=0.01, outlier_scale=50.0)
+    xf = inputs.bf16_bits_to_f32(x)
+    for abits, Qb in [(4, 7), (8, 127)]:
+        q, deq, r = orc.quantize_activations(x, abits, use_h=True, norm=True)
+        u = (xf * r[:, None]).astype(np.float32)
+        z = (orc.fwht_f32(u) * np.float32(1.0 / math.sqrt(K))).astype(np.float32)
+        g = np.abs(z).max(axis=1).astype(np.float32)
+        s = (np.float32(Qb) / g).astype(np.float32)
+        qt = np.clip(np.rint((z * s[:, None]).astype(np.float32)), -Qb - 1, Qb).astype(np.int8)
+        deqt = (g / np.float32(Qb)).astype(np.float32)
+        assert float((qt != q).mean()) <= 1e-4
+        assert int(np.abs(qt.astype(np.int32) - q).max()) <= 1
+        np.testing.assert_allclose(deqt, deq, rtol=1e-6)
