@@ -1,0 +1,180 @@
+"""Thin Python binding of libhbl (the C ABI in include/hbl.h).
+
+Argument marshalling only: torch tensors provide device memory and the current HIP stream;
+every step of the layer runs in libhbl's HIP kernels.  There is no fallback: if the
+library is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libhbl.so")
+
+HBL_OK, HBL_ERR_INVALID_ARG, HBL_ERR_UNSUPPORTED, HBL_ERR_WORKSPACE, HBL_ERR_HIP = range(5)
+HBL_F32, HBL_BF16 = 0, 1
+HBL_NORM_NONE, HBL_NORM_RMS = 0, 1
+
+_lock = threading.Lock()
+_lib = None
+
+
+class HBLError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Loads libhbl.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m bit_quantized_gemm_bitlinear_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, I, F, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        sig = {
+            "hbl_packed_weight_bytes": (SZ, [I64, I64]),
+            "hbl_packed_act_bytes": (SZ, [I64, I64, I]),
+            "hbl_wquant_workspace_bytes": (SZ, [I64, I64]),
+            "hbl_forward_workspace_bytes": (SZ, [I64, I64, I]),
+            "hbl_quantize_weights": (I, [P, I64, I64, P, P, P, SZ, P]),
+            "hbl_quantize_activations": (I, [P, I, I64, I64, I, P, F, I, I, P, P, P]),
+            "hbl_gemm_s32": (I, [P, P, I64, I64, I64, I, P, P]),
+            "hbl_gemm_dequant": (I, [P, P, P, P, I64, I64, I64, I, P, P]),
+            "hbl_forward": (I, [P, I, P, P, I64, I64, I64, I, I, I, P, F, P, P, SZ, P]),
+            "hbl_swiglu": (I, [P, P, I64, P, P]),
+            "hbl_status_string": (ctypes.c_char_p, [I]),
+            "hbl_last_error": (ctypes.c_char_p, []),
+            "hbl_version": (I, []),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+        return L
+
+
+def _check(status: int) -> None:
+    if status != HBL_OK:
+        L = lib()
+        raise HBLError(status, f"{L.hbl_status_string(status).decode()}: {L.hbl_last_error().decode()}")
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream():
+    import torch
+
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _xdtype(x) -> int:
+    import torch
+
+    if x.dtype == torch.bfloat16:
+        return HBL_BF16
+    if x.dtype == torch.float32:
+        return HBL_F32
+    raise TypeError("activations must be torch.bfloat16 or torch.float32")
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous and on the GPU")
+
+
+def quantize_weights(W):
+    """W [N, K] fp32 on the GPU -> (Wq uint8 [N, K/4], w_scale fp32 [1])."""
+    import torch
+
+    _dev(W)
+    N, K = W.shape
+    L = lib()
+    Wq = torch.empty((N, K // 4), dtype=torch.uint8, device=W.device)
+    scale = torch.empty(1, dtype=torch.float32, device=W.device)
+    wsb = L.hbl_wquant_workspace_bytes(N, K)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=W.device)
+    _check(L.hbl_quantize_weights(_ptr(W), N, K, _ptr(Wq), _ptr(scale), _ptr(ws), ws.numel(), _stream()))
+    return Wq, scale
+
+
+def quantize_activations(x, abits: int, use_hadamard: bool, norm: bool = False, gamma=None, eps: float = 1e-5):
+    """x [M, K] bf16/fp32 -> (codes uint8 [M, K*abits/8], deq fp32 [M])."""
+    import torch
+
+    _dev(x, gamma)
+    M, K = x.shape
+    codes = torch.empty((M, K * abits // 8), dtype=torch.uint8, device=x.device)
+    deq = torch.empty(M, dtype=torch.float32, device=x.device)
+    _check(lib().hbl_quantize_activations(_ptr(x), _xdtype(x), M, K, HBL_NORM_RMS if norm else HBL_NORM_NONE,
+                                          _ptr(gamma), float(eps), int(abits), int(bool(use_hadamard)),
+                                          _ptr(codes), _ptr(deq), _stream()))
+    return codes, deq
+
+
+def gemm_s32(codes, Wq, K: int, abits: int):
+    """codes [M, K*abits/8], Wq [N, K/4] -> acc int32 [M, N] (exact integer product)."""
+    import torch
+
+    _dev(codes, Wq)
+    M, N = codes.shape[0], Wq.shape[0]
+    acc = torch.empty((M, N), dtype=torch.int32, device=codes.device)
+    _check(lib().hbl_gemm_s32(_ptr(codes), _ptr(Wq), M, K, N, int(abits), _ptr(acc), _stream()))
+    return acc
+
+
+def gemm_dequant(codes, deq, Wq, w_scale, K: int, abits: int, y=None):
+    import torch
+
+    _dev(codes, deq, Wq, w_scale, y)
+    M, N = codes.shape[0], Wq.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=codes.device)
+    _check(lib().hbl_gemm_dequant(_ptr(codes), _ptr(deq), _ptr(Wq), _ptr(w_scale), M, K, N, int(abits), _ptr(y),
+                                  _stream()))
+    return y
+
+
+def forward_workspace(M: int, K: int, abits: int, device="cuda"):
+    import torch
+
+    n = lib().hbl_forward_workspace_bytes(M, K, abits)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def forward(x, Wq, w_scale, abits: int, use_hadamard: bool, norm: bool = False, gamma=None, eps: float = 1e-5,
+            y=None, ws=None):
+    """The whole (H-)BitLinear forward: x [M, K] -> y fp32 [M, N]."""
+    import torch
+
+    _dev(x, Wq, w_scale, gamma, y, ws)
+    M, K = x.shape
+    N = Wq.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = forward_workspace(M, K, abits, x.device)
+    _check(lib().hbl_forward(_ptr(x), _xdtype(x), _ptr(Wq), _ptr(w_scale), M, K, N, int(abits),
+                             int(bool(use_hadamard)), HBL_NORM_RMS if norm else HBL_NORM_NONE, _ptr(gamma),
+                             float(eps), _ptr(y), _ptr(ws), ws.numel(), _stream()))
+    return y
+
+
+def swiglu(g, u, h=None):
+    import torch
+
+    _dev(g, u, h)
+    if h is None:
+        h = torch.empty_like(g)
+    _check(lib().hbl_swiglu(_ptr(g), _ptr(u), g.numel(), _ptr(h), _stream()))
+    return h

@@ -1,0 +1,235 @@
+// api.cpp — the C ABI of libhbl (declared in include/hbl.h): synchronous argument
+// validation, workspace carving and dispatch to the HIP kernels.  No HIP call happens
+// before every argument has been checked, so validation is testable on a host without a
+// GPU.  No exception crosses the ABI.
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "hbl.h"
+#include "hbl_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+hbl_status fail(hbl_status s, const char* fn, const std::string& what) {
+  g_last_error = std::string(fn) + ": " + what;
+  return s;
+}
+
+hbl_status hip_fail(const char* fn, hipError_t e) {
+  g_last_error = std::string(fn) + ": HIP error " + hipGetErrorName(e) + " (" + hipGetErrorString(e) + ")";
+  return HBL_ERR_HIP;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
+
+// Shared checks of (M, K, N, abits).  N < 0 means "no N in this call".
+hbl_status check_shape(const char* fn, int64_t M, int64_t K, int64_t N, int abits) {
+  if (M < 0 || M > INT32_MAX) return fail(HBL_ERR_INVALID_ARG, fn, "M must be in [0, 2^31)");
+  if (N != -1 && (N < 1 || N > INT32_MAX)) return fail(HBL_ERR_INVALID_ARG, fn, "N must be in [1, 2^31)");
+  if (K < 64 || K % 64 != 0) return fail(HBL_ERR_INVALID_ARG, fn, "K must be a positive multiple of 64");
+  if (K > HBL_MAX_K) return fail(HBL_ERR_UNSUPPORTED, fn, "K above HBL_MAX_K");
+  if (abits != 4 && abits != 8) return fail(HBL_ERR_INVALID_ARG, fn, "abits must be 4 or 8");
+  if (M * K > INT64_MAX / 8) return fail(HBL_ERR_INVALID_ARG, fn, "M*K too large");
+  return HBL_OK;
+}
+
+hbl_status check_ptr(const char* fn, const void* p, const char* name, uintptr_t align) {
+  if (p == nullptr) return fail(HBL_ERR_INVALID_ARG, fn, std::string(name) + " is NULL");
+  if (!aligned(p, align))
+    return fail(HBL_ERR_INVALID_ARG, fn, std::string(name) + " is not " + std::to_string(align) + "-byte aligned");
+  return HBL_OK;
+}
+
+hbl_status check_act(const char* fn, hbl_dtype xt, hbl_norm norm, const float* gamma, float eps, int use_h,
+                     int64_t K) {
+  if (xt != HBL_F32 && xt != HBL_BF16) return fail(HBL_ERR_INVALID_ARG, fn, "unknown activation dtype");
+  if (norm != HBL_NORM_NONE && norm != HBL_NORM_RMS) return fail(HBL_ERR_INVALID_ARG, fn, "unknown norm");
+  if (norm == HBL_NORM_RMS && !(std::isfinite(eps) && eps >= 0.0f))
+    return fail(HBL_ERR_INVALID_ARG, fn, "norm_eps must be finite and >= 0");
+  if (norm == HBL_NORM_RMS && gamma != nullptr && !aligned(gamma, 16))
+    return fail(HBL_ERR_INVALID_ARG, fn, "gamma is not 16-byte aligned");
+  if (use_h != 0 && use_h != 1) return fail(HBL_ERR_INVALID_ARG, fn, "use_hadamard must be 0 or 1");
+  if (use_h && !pow2(K)) return fail(HBL_ERR_UNSUPPORTED, fn, "the Hadamard transform needs K a power of two");
+  if (use_h && K > HBL_MAX_K_HADAMARD) return fail(HBL_ERR_UNSUPPORTED, fn, "K above HBL_MAX_K_HADAMARD");
+  return HBL_OK;
+}
+
+#define HBL_TRY(expr)              \
+  do {                             \
+    hbl_status st_ = (expr);       \
+    if (st_ != HBL_OK) return st_; \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int hbl_version(void) { return 100; }
+
+const char* hbl_status_string(hbl_status s) {
+  switch (s) {
+    case HBL_OK: return "HBL_OK";
+    case HBL_ERR_INVALID_ARG: return "HBL_ERR_INVALID_ARG";
+    case HBL_ERR_UNSUPPORTED: return "HBL_ERR_UNSUPPORTED";
+    case HBL_ERR_WORKSPACE: return "HBL_ERR_WORKSPACE";
+    case HBL_ERR_HIP: return "HBL_ERR_HIP";
+  }
+  return "HBL_ERR_UNKNOWN";
+}
+
+const char* hbl_last_error(void) { return g_last_error.c_str(); }
+
+size_t hbl_packed_weight_bytes(int64_t N, int64_t K) {
+  if (N < 1 || K < 64 || K % 64 != 0 || K > HBL_MAX_K || N > INT32_MAX) return 0;
+  return (size_t)(N * (K / 4));
+}
+
+size_t hbl_packed_act_bytes(int64_t M, int64_t K, int abits) {
+  if (M < 0 || K < 64 || K % 64 != 0 || K > HBL_MAX_K || M > INT32_MAX || (abits != 4 && abits != 8)) return 0;
+  return (size_t)(M * K * abits / 8);
+}
+
+size_t hbl_wquant_workspace_bytes(int64_t N, int64_t K) {
+  if (N < 1 || K < 64 || K % 64 != 0 || K > HBL_MAX_K || N > INT32_MAX) return 0;
+  return (size_t)N * sizeof(double);
+}
+
+size_t hbl_forward_workspace_bytes(int64_t M, int64_t K, int abits) {
+  if (M < 0 || K < 64 || K % 64 != 0 || K > HBL_MAX_K || M > INT32_MAX || (abits != 4 && abits != 8)) return 0;
+  return round256((size_t)(M * K * abits / 8)) + round256((size_t)M * sizeof(float));
+}
+
+hbl_status hbl_quantize_weights(const float* W, int64_t N, int64_t K, uint8_t* Wq, float* w_scale, void* ws,
+                                size_t ws_bytes, void* stream) {
+  static const char* fn = "hbl_quantize_weights";
+  try {
+    if (N < 1 || N > INT32_MAX) return fail(HBL_ERR_INVALID_ARG, fn, "N must be in [1, 2^31)");
+    HBL_TRY(check_shape(fn, 0, K, N, 4));
+    HBL_TRY(check_ptr(fn, W, "W", 16));
+    HBL_TRY(check_ptr(fn, Wq, "Wq", 16));
+    HBL_TRY(check_ptr(fn, w_scale, "w_scale", 4));
+    if (ws == nullptr || ws_bytes < hbl_wquant_workspace_bytes(N, K))
+      return fail(HBL_ERR_WORKSPACE, fn, "workspace missing or smaller than hbl_wquant_workspace_bytes");
+    HBL_TRY(check_ptr(fn, ws, "ws", 16));
+    hipError_t e = hbl::launch_wquant(W, N, K, Wq, w_scale, static_cast<double*>(ws), (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return HBL_OK;
+  } catch (...) {
+    return fail(HBL_ERR_HIP, fn, "unexpected C++ exception");
+  }
+}
+
+hbl_status hbl_quantize_activations(const void* x, hbl_dtype xt, int64_t M, int64_t K, hbl_norm norm,
+                                    const float* gamma, float norm_eps, int abits, int use_hadamard, uint8_t* codes,
+                                    float* deq, void* stream) {
+  static const char* fn = "hbl_quantize_activations";
+  try {
+    HBL_TRY(check_shape(fn, M, K, -1, abits));
+    HBL_TRY(check_act(fn, xt, norm, gamma, norm_eps, use_hadamard, K));
+    if (M == 0) return HBL_OK;
+    HBL_TRY(check_ptr(fn, x, "x", 16));
+    HBL_TRY(check_ptr(fn, codes, "codes", 16));
+    HBL_TRY(check_ptr(fn, deq, "deq", 4));
+    hipError_t e = hbl::launch_actquant(x, (int)xt, M, K, (int)norm, norm == HBL_NORM_RMS ? gamma : nullptr,
+                                        norm_eps, abits, use_hadamard, codes, deq, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return HBL_OK;
+  } catch (...) {
+    return fail(HBL_ERR_HIP, fn, "unexpected C++ exception");
+  }
+}
+
+hbl_status hbl_gemm_s32(const uint8_t* codes, const uint8_t* Wq, int64_t M, int64_t K, int64_t N, int abits,
+                        int32_t* acc, void* stream) {
+  static const char* fn = "hbl_gemm_s32";
+  try {
+    HBL_TRY(check_shape(fn, M, K, N, abits));
+    HBL_TRY(check_ptr(fn, Wq, "Wq", 16));
+    if (M == 0) return HBL_OK;
+    HBL_TRY(check_ptr(fn, codes, "codes", 16));
+    HBL_TRY(check_ptr(fn, acc, "acc", 16));
+    hipError_t e = hbl::launch_gemm(codes, nullptr, Wq, nullptr, M, K, N, abits, acc, nullptr, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return HBL_OK;
+  } catch (...) {
+    return fail(HBL_ERR_HIP, fn, "unexpected C++ exception");
+  }
+}
+
+hbl_status hbl_gemm_dequant(const uint8_t* codes, const float* deq, const uint8_t* Wq, const float* w_scale,
+                            int64_t M, int64_t K, int64_t N, int abits, float* y, void* stream) {
+  static const char* fn = "hbl_gemm_dequant";
+  try {
+    HBL_TRY(check_shape(fn, M, K, N, abits));
+    HBL_TRY(check_ptr(fn, Wq, "Wq", 16));
+    HBL_TRY(check_ptr(fn, w_scale, "w_scale", 4));
+    if (M == 0) return HBL_OK;
+    HBL_TRY(check_ptr(fn, codes, "codes", 16));
+    HBL_TRY(check_ptr(fn, deq, "deq", 4));
+    HBL_TRY(check_ptr(fn, y, "y", 16));
+    hipError_t e = hbl::launch_gemm(codes, deq, Wq, w_scale, M, K, N, abits, nullptr, y, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return HBL_OK;
+  } catch (...) {
+    return fail(HBL_ERR_HIP, fn, "unexpected C++ exception");
+  }
+}
+
+hbl_status hbl_forward(const void* x, hbl_dtype xt, const uint8_t* Wq, const float* w_scale, int64_t M, int64_t K,
+                       int64_t N, int abits, int use_hadamard, hbl_norm norm, const float* gamma, float norm_eps,
+                       float* y, void* ws, size_t ws_bytes, void* stream) {
+  static const char* fn = "hbl_forward";
+  try {
+    HBL_TRY(check_shape(fn, M, K, N, abits));
+    HBL_TRY(check_act(fn, xt, norm, gamma, norm_eps, use_hadamard, K));
+    HBL_TRY(check_ptr(fn, Wq, "Wq", 16));
+    HBL_TRY(check_ptr(fn, w_scale, "w_scale", 4));
+    if (M == 0) return HBL_OK;
+    HBL_TRY(check_ptr(fn, x, "x", 16));
+    HBL_TRY(check_ptr(fn, y, "y", 16));
+    const size_t need = hbl_forward_workspace_bytes(M, K, abits);
+    if (ws == nullptr || ws_bytes < need)
+      return fail(HBL_ERR_WORKSPACE, fn, "workspace missing or smaller than hbl_forward_workspace_bytes");
+    HBL_TRY(check_ptr(fn, ws, "ws", 256));
+    uint8_t* codes = static_cast<uint8_t*>(ws);
+    float* deq = reinterpret_cast<float*>(codes + round256((size_t)(M * K * abits / 8)));
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = hbl::launch_actquant(x, (int)xt, M, K, (int)norm, norm == HBL_NORM_RMS ? gamma : nullptr,
+                                        norm_eps, abits, use_hadamard, codes, deq, s);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    e = hbl::launch_gemm(codes, deq, Wq, w_scale, M, K, N, abits, nullptr, y, s);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return HBL_OK;
+  } catch (...) {
+    return fail(HBL_ERR_HIP, fn, "unexpected C++ exception");
+  }
+}
+
+hbl_status hbl_swiglu(const float* g, const float* u, int64_t n, float* h, void* stream) {
+  static const char* fn = "hbl_swiglu";
+  try {
+    if (n < 0) return fail(HBL_ERR_INVALID_ARG, fn, "n must be >= 0");
+    if (n == 0) return HBL_OK;
+    HBL_TRY(check_ptr(fn, g, "g", 16));
+    HBL_TRY(check_ptr(fn, u, "u", 16));
+    HBL_TRY(check_ptr(fn, h, "h", 16));
+    const uintptr_t hb = reinterpret_cast<uintptr_t>(h), he = hb + (uintptr_t)n * sizeof(float);
+    for (const float* p : {g, u}) {
+      const uintptr_t pb = reinterpret_cast<uintptr_t>(p), pe = pb + (uintptr_t)n * sizeof(float);
+      if (hb < pe && pb < he) return fail(HBL_ERR_INVALID_ARG, fn, "h overlaps an input");
+    }
+    hipError_t e = hbl::launch_swiglu(g, u, n, h, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return HBL_OK;
+  } catch (...) {
+    return fail(HBL_ERR_HIP, fn, "unexpected C++ exception");
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,49 @@
+// hbl_device.h — device helpers shared by the HIP kernels of libhbl (gfx950 only).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hbl {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+// bf16 bit patterns live in the top half of an fp32 word; the conversion is exact.
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Round half to even then convert (v_rndne_f32 + v_cvt_i32_f32).
+__device__ __forceinline__ int rne_int(float v) { return (int)__builtin_rintf(v); }
+
+// Eight consecutive INT4 codes c[0..7] (k = 8h + 0..7 of a 16-code group) -> one 32-bit
+// word of the packed INT4 layout: byte i holds c[i] (low nibble) and c[i+4] (high nibble).
+__device__ __forceinline__ uint32_t pack8_a4(int c0, int c1, int c2, int c3, int c4, int c5, int c6,
+                                             int c7) {
+  uint32_t b0 = (uint32_t)(c0 & 15) | ((uint32_t)(c4 & 15) << 4);
+  uint32_t b1 = (uint32_t)(c1 & 15) | ((uint32_t)(c5 & 15) << 4);
+  uint32_t b2 = (uint32_t)(c2 & 15) | ((uint32_t)(c6 & 15) << 4);
+  uint32_t b3 = (uint32_t)(c3 & 15) | ((uint32_t)(c7 & 15) << 4);
+  return b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+}
+
+// Four consecutive INT8 codes -> one little-endian word.
+__device__ __forceinline__ uint32_t pack4_a8(int c0, int c1, int c2, int c3) {
+  return (uint32_t)(c0 & 255) | ((uint32_t)(c1 & 255) << 8) | ((uint32_t)(c2 & 255) << 16) |
+         ((uint32_t)(c3 & 255) << 24);
+}
+
+// Butterfly reductions across the lanes of a wave (width = power of two <= 64).
+template <int WIDTH>
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = WIDTH / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+template <int WIDTH>
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int o = WIDTH / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+}  // namespace hbl

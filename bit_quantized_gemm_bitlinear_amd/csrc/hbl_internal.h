@@ -1,0 +1,26 @@
+// hbl_internal.h — launchers implemented by the kernel translation units and called by
+// the C ABI layer (api.cpp) after argument validation.  Each returns hipSuccess or the
+// launch error.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hbl {
+
+// Weight ternarisation (k_wquant.hip).  ws: N doubles.
+hipError_t launch_wquant(const float* W, int64_t N, int64_t K, uint8_t* Wq, float* w_scale, double* ws,
+                         hipStream_t s);
+
+// Activation quantisation (k_actquant.hip).  xt: 0 fp32, 1 bf16.
+hipError_t launch_actquant(const void* x, int xt, int64_t M, int64_t K, int norm, const float* gamma,
+                           float eps, int abits, int use_h, uint8_t* codes, float* deq, hipStream_t s);
+
+// Integer GEMM with either an int32 output (acc != nullptr) or the dequantising epilogue
+// (y != nullptr) (k_gemm.hip).
+hipError_t launch_gemm(const uint8_t* codes, const float* deq, const uint8_t* Wq, const float* w_scale,
+                       int64_t M, int64_t K, int64_t N, int abits, int32_t* acc, float* y, hipStream_t s);
+
+// h = silu(g) * u (k_swiglu.hip).
+hipError_t launch_swiglu(const float* g, const float* u, int64_t n, float* h, hipStream_t s);
+
+}  // namespace hbl

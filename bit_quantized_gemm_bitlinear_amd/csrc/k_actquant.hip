@@ -1,0 +1,468 @@
+// k_actquant.hip — fused per-token activation path of H-BitLinear:
+//   load (bf16/fp32) -> RMSNorm statistics -> online fast Walsh-Hadamard transform ->
+//   per-token absmax -> INT4/INT8 codes -> packed store + one dequant factor per row.
+//
+// BitNet v2 write-up, section H-BitLinear模塊: before the activations are quantised the
+// layer applies LN and an online Hadamard transform computed with the fast Hadamard
+// transform (O(n log n)); the transform reshapes the outlier-heavy inputs of Wo / Wdown
+// into a Gaussian-like distribution; the activations are then quantised per token to INT8
+// or INT4.  bitnet.cpp article, section "6 页论文，引入 1 bit LLM": activations are scaled
+// into [-Qb, Qb] without a zero point.
+//
+// Transform (use_hadamard = 1, K = 2^L, 6 <= L <= 15).  Every thread owns 64 values of one
+// row.  The butterfly stages run strictly in ascending order of the index bit they act on
+// (h = 1, 2, 4, ..., K/2), so the fp32 result is bit-identical to the plain in-place loop.
+// A stage always acts on a register bit of the current layout; between groups of stages the
+// row is transposed through LDS so that the next index bits become register bits:
+//   phase 0: registers = index bits 0..5 (64 consecutive elements, loaded from HBM)
+//   later phases: registers = the next active index bits + the lowest index bits, so the
+//   last phase leaves runs of >= 8 consecutive elements in registers, ready to be packed
+//   and stored without another transpose.
+// LDS rows are padded with 4 floats every 64 (the padded address is linear in disjoint
+// index bits, so every register offset is a compile-time immediate).
+//
+// The RMSNorm factor r and 1/sqrt(K) are not applied to the values: absmax codes do not
+// change under a positive per-row scale, so both are folded into deq.
+#include <cmath>
+
+#include "hbl_device.h"
+#include "hbl_internal.h"
+
+namespace hbl {
+namespace {
+
+struct PhaseDesc {
+  int lo;  // first active index bit
+  int a;   // number of active index bits (butterfly stages) in this phase
+};
+
+constexpr int nphases(int L) { return L <= 6 ? 1 : (L <= 9 ? 2 : 3); }
+
+constexpr PhaseDesc phase_desc(int L, int p) {
+  if (p == 0) return PhaseDesc{0, L < 6 ? L : 6};
+  if (L <= 9) return PhaseDesc{6, L - 6};
+  if (L <= 12) return p == 1 ? PhaseDesc{6, L - 9} : PhaseDesc{L - 3, 3};
+  return p == 1 ? PhaseDesc{6, 6} : PhaseDesc{12, L - 12};
+}
+
+// Register j of a thread in phase P holds row element  base(t) + off(j):
+//   j's low c = 6-a bits -> index bits 0..c-1 ; j's high a bits -> index bits lo..lo+a-1;
+//   the thread index t fills the remaining index bits in ascending order.
+template <int L, int P>
+struct Layout {
+  static constexpr PhaseDesc d = phase_desc(L, P);
+  static constexpr int a = d.a;
+  static constexpr int lo = d.lo;
+  static constexpr int c = 6 - d.a;
+  static __device__ __forceinline__ constexpr int off(int j) {
+    return (j & ((1 << c) - 1)) | ((j >> c) << lo);
+  }
+  static __device__ __forceinline__ int base(int t) {
+    return ((t & ((1 << (lo - c)) - 1)) << c) | ((t >> (lo - c)) << (lo + a));
+  }
+};
+
+__device__ __forceinline__ constexpr int padded(int i) { return i + ((i >> 6) << 2); }
+
+// Butterfly stages on register bits [c, c + a) in ascending order.
+template <int C, int A>
+__device__ __forceinline__ void stages(float (&v)[64]) {
+#pragma unroll
+  for (int s = 0; s < A; ++s) {
+    const int h = 1 << (C + s);
+#pragma unroll
+    for (int j = 0; j < 64; ++j) {
+      if ((j & h) == 0) {
+        float x0 = v[j], x1 = v[j + h];
+        v[j] = x0 + x1;
+        v[j + h] = x0 - x1;
+      }
+    }
+  }
+}
+
+// Row-wide reductions for rows spread over T threads (T a power of two).  Threads of a
+// row are contiguous in the block; rows of <= 64 threads stay inside one wave.
+template <int T>
+__device__ __forceinline__ float row_max(float v, float* red) {
+  if constexpr (T <= 64) {
+    return wave_max<T>(v);
+  } else {
+    v = wave_max<64>(v);
+    const int tid = threadIdx.x;
+    if ((tid & 63) == 0) red[tid >> 6] = v;
+    __syncthreads();
+    const int w0 = (tid / T) * (T / 64);
+    float m = red[w0];
+#pragma unroll
+    for (int i = 1; i < T / 64; ++i) m = fmaxf(m, red[w0 + i]);
+    return m;
+  }
+}
+
+template <int T>
+__device__ __forceinline__ double row_sum(double v, double* red) {
+  if constexpr (T <= 64) {
+    return wave_sum<T>(v);
+  } else {
+    v = wave_sum<64>(v);
+    const int tid = threadIdx.x;
+    if ((tid & 63) == 0) red[tid >> 6] = v;
+    __syncthreads();
+    const int w0 = (tid / T) * (T / 64);
+    double s = red[w0];
+#pragma unroll
+    for (int i = 1; i < T / 64; ++i) s += red[w0 + i];
+    return s;
+  }
+}
+
+template <int ABITS>
+struct QB {
+  static constexpr float value = ABITS == 4 ? 7.0f : 127.0f;
+};
+
+// Store NWORDS packed 32-bit words to dst (aligned to 4 * min(NWORDS, 4) bytes).
+template <int NWORDS>
+__device__ __forceinline__ void store_words(uint8_t* dst, const uint32_t* w) {
+  if constexpr (NWORDS >= 4) {
+#pragma unroll
+    for (int d = 0; d < NWORDS; d += 4)
+      *reinterpret_cast<uint4*>(dst + 4 * d) = make_uint4(w[d], w[d + 1], w[d + 2], w[d + 3]);
+  } else if constexpr (NWORDS == 2) {
+    *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+  } else {
+    *reinterpret_cast<uint32_t*>(dst) = w[0];
+  }
+}
+
+// Quantise a run of RL consecutive row elements v[0 .. RL) starting at row element k0 and
+// store its packed bytes (INT4: 8 codes per word at byte k0/2; INT8: 4 codes per word).
+template <int ABITS, int RL>
+__device__ __forceinline__ void store_run(const float* v, float s, uint8_t* __restrict__ crow, int k0) {
+  if constexpr (ABITS == 4) {
+    uint32_t w[RL / 8];
+#pragma unroll
+    for (int d = 0; d < RL / 8; ++d)
+      w[d] = pack8_a4(rne_int(v[8 * d + 0] * s), rne_int(v[8 * d + 1] * s), rne_int(v[8 * d + 2] * s),
+                      rne_int(v[8 * d + 3] * s), rne_int(v[8 * d + 4] * s), rne_int(v[8 * d + 5] * s),
+                      rne_int(v[8 * d + 6] * s), rne_int(v[8 * d + 7] * s));
+    store_words<RL / 8>(crow + k0 / 2, w);
+  } else {
+    uint32_t w[RL / 4];
+#pragma unroll
+    for (int d = 0; d < RL / 4; ++d)
+      w[d] = pack4_a8(rne_int(v[4 * d + 0] * s), rne_int(v[4 * d + 1] * s), rne_int(v[4 * d + 2] * s),
+                      rne_int(v[4 * d + 3] * s));
+    store_words<RL / 4>(crow + k0, w);
+  }
+}
+
+template <int L, int P, int ROWF>
+__device__ __forceinline__ void lds_read(float (&v)[64], const float* rowlds, int t) {
+  using LY = Layout<L, P>;
+  const float* b = rowlds + padded(LY::base(t));
+#pragma unroll
+  for (int j = 0; j < 64; ++j) v[j] = b[padded(LY::off(j))];
+}
+
+template <int L, int P, int ROWF>
+__device__ __forceinline__ void lds_write(const float (&v)[64], float* rowlds, int t) {
+  using LY = Layout<L, P>;
+  float* b = rowlds + padded(LY::base(t));
+#pragma unroll
+  for (int j = 0; j < 64; ++j) b[padded(LY::off(j))] = v[j];
+}
+
+template <int L>
+constexpr int block_threads() {
+  return (1 << L) / 64 > 256 ? (1 << L) / 64 : 256;
+}
+
+template <int L, int ABITS, int XT>
+__global__ __launch_bounds__(block_threads<L>()) void k_actquant_h(
+    const void* __restrict__ x, int64_t M, const float* __restrict__ gamma, float eps, int norm, float hK,
+    uint8_t* __restrict__ codes, float* __restrict__ deq) {
+  constexpr int K = 1 << L;
+  constexpr int T = K / 64;           // threads per row
+  constexpr int WG = block_threads<L>();
+  constexpr int R = WG / T;           // rows per block
+  constexpr int NP = nphases(L);
+  constexpr int ROWF = K + K / 16;    // padded floats per LDS row
+  constexpr int NW = WG / 64;
+  __shared__ float lds[NP > 1 ? R * ROWF : 1];
+  __shared__ float redf[NW];
+  __shared__ double redd[NW];
+
+  const int tid = threadIdx.x;
+  const int rl = tid / T;
+  const int t = tid % T;
+  const int64_t row = (int64_t)blockIdx.x * R + rl;
+  const bool valid = row < M;
+
+  float v[64];
+  if (valid) {
+    if constexpr (XT == 1) {
+      const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + row * K + 64 * t);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        uint4 w = src[i];
+        v[8 * i + 0] = bf16lo(w.x);
+        v[8 * i + 1] = bf16hi(w.x);
+        v[8 * i + 2] = bf16lo(w.y);
+        v[8 * i + 3] = bf16hi(w.y);
+        v[8 * i + 4] = bf16lo(w.z);
+        v[8 * i + 5] = bf16hi(w.z);
+        v[8 * i + 6] = bf16lo(w.w);
+        v[8 * i + 7] = bf16hi(w.w);
+      }
+    } else {
+      const float4* src = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + row * K + 64 * t);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float4 f = src[i];
+        v[4 * i + 0] = f.x;
+        v[4 * i + 1] = f.y;
+        v[4 * i + 2] = f.z;
+        v[4 * i + 3] = f.w;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 64; ++j) v[j] = 0.0f;
+  }
+
+  float r = 1.0f;
+  if (norm) {
+    double ss = 0.0;
+#pragma unroll
+    for (int j = 0; j < 64; ++j) ss = __builtin_fma((double)v[j], (double)v[j], ss);  // x^2 is exact in fp64
+    ss = row_sum<T>(ss, redd);
+    r = (float)(1.0 / sqrt(ss / (double)K + (double)eps));
+    if (gamma != nullptr) {
+      const float4* gp = reinterpret_cast<const float4*>(gamma + 64 * t);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float4 g = gp[i];
+        v[4 * i + 0] *= g.x;
+        v[4 * i + 1] *= g.y;
+        v[4 * i + 2] *= g.z;
+        v[4 * i + 3] *= g.w;
+      }
+    }
+  }
+
+  // Phase 0: index bits 0..5 in registers.
+  stages<0, phase_desc(L, 0).a>(v);
+  float* rowlds = lds + rl * ROWF;
+  if constexpr (NP > 1) {
+    lds_write<L, 0, ROWF>(v, rowlds, t);
+    __syncthreads();
+    lds_read<L, 1, ROWF>(v, rowlds, t);
+    stages<Layout<L, 1>::c, Layout<L, 1>::a>(v);
+  }
+  if constexpr (NP > 2) {
+    lds_write<L, 1, ROWF>(v, rowlds, t);
+    __syncthreads();
+    lds_read<L, 2, ROWF>(v, rowlds, t);
+    stages<Layout<L, 2>::c, Layout<L, 2>::a>(v);
+  }
+
+  float amax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 64; ++j) amax = fmaxf(amax, fabsf(v[j]));
+  amax = row_max<T>(amax, redf);
+
+  if (!valid) return;
+  constexpr float Qb = QB<ABITS>::value;
+  uint8_t* crow = codes + row * (int64_t)(K * ABITS / 8);
+  constexpr int LASTP = NP - 1;
+  using LY = Layout<L, LASTP>;
+  constexpr int RL = NP == 1 ? 64 : (1 << LY::c);  // run of consecutive elements in registers
+  const int b = NP == 1 ? 0 : LY::base(t);
+  float dq = 0.0f;
+  if (amax < 0x1p-120f) {
+    const float zero[64] = {};
+#pragma unroll
+    for (int g = 0; g < 64 / RL; ++g) store_run<ABITS, RL>(zero + g * RL, 0.0f, crow, NP == 1 ? 64 * t : b + LY::off(g * RL));
+  } else {
+    const float s = Qb / amax;
+#pragma unroll
+    for (int g = 0; g < 64 / RL; ++g) store_run<ABITS, RL>(v + g * RL, s, crow, NP == 1 ? 64 * t : b + LY::off(g * RL));
+    dq = __fmul_rn(__fmul_rn(amax / Qb, r), hK);
+  }
+  if (t == 0) deq[row] = dq;
+}
+
+// BitLinear path (no transform), any K with K % 64 == 0: one 256-thread block per row,
+// the row held in registers as NCH chunks of 8 consecutive elements per thread
+// (K <= 2048 * NCH), or streamed twice from memory when NCH == 0.
+template <int ABITS, int XT, int NCH>
+__global__ __launch_bounds__(256) void k_actquant_plain(const void* __restrict__ x, int64_t M, int64_t K,
+                                                        const float* __restrict__ gamma, float eps, int norm,
+                                                        uint8_t* __restrict__ codes, float* __restrict__ deq) {
+  constexpr int NCHR = NCH > 0 ? NCH : 1;
+  __shared__ float redf[4];
+  __shared__ double redd[4];
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int nch = (int)(K / 8);
+  auto load8 = [&](int ch, float* o) {
+    if constexpr (XT == 1) {
+      uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + row * K + 8 * ch);
+      o[0] = bf16lo(w.x); o[1] = bf16hi(w.x); o[2] = bf16lo(w.y); o[3] = bf16hi(w.y);
+      o[4] = bf16lo(w.z); o[5] = bf16hi(w.z); o[6] = bf16lo(w.w); o[7] = bf16hi(w.w);
+    } else {
+      const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + row * K + 8 * ch);
+      float4 a = p[0], b = p[1];
+      o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w; o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+    }
+  };
+  auto scale8 = [&](int ch, float* o) {
+    if (norm && gamma != nullptr) {
+      const float4* gp = reinterpret_cast<const float4*>(gamma + 8 * ch);
+      float4 a = gp[0], b = gp[1];
+      o[0] *= a.x; o[1] *= a.y; o[2] *= a.z; o[3] *= a.w; o[4] *= b.x; o[5] *= b.y; o[6] *= b.z; o[7] *= b.w;
+    }
+  };
+  float v[NCHR][8];
+  double ss = 0.0;
+  float amax = 0.0f;
+  if constexpr (NCH > 0) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int ch = tid + 256 * c;
+      if (ch < nch) {
+        load8(ch, v[c]);
+        if (norm) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ss = __builtin_fma((double)v[c][e], (double)v[c][e], ss);
+        }
+        scale8(ch, v[c]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[c][e]));
+      }
+    }
+  } else {
+    for (int ch = tid; ch < nch; ch += 256) {
+      float o[8];
+      load8(ch, o);
+      if (norm) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss = __builtin_fma((double)o[e], (double)o[e], ss);
+      }
+      scale8(ch, o);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(o[e]));
+    }
+  }
+  float r = 1.0f;
+  if (norm) {
+    ss = row_sum<256>(ss, redd);
+    r = (float)(1.0 / sqrt(ss / (double)K + (double)eps));
+  }
+  amax = row_max<256>(amax, redf);
+  constexpr float Qb = QB<ABITS>::value;
+  const bool zero = amax < 0x1p-120f;
+  const float s = zero ? 0.0f : Qb / amax;
+  uint8_t* crow = codes + row * (K * ABITS / 8);
+  auto put = [&](int ch, const float* o) {
+    if constexpr (ABITS == 4) {
+      *reinterpret_cast<uint32_t*>(crow + 4 * ch) =
+          pack8_a4(rne_int(o[0] * s), rne_int(o[1] * s), rne_int(o[2] * s), rne_int(o[3] * s),
+                   rne_int(o[4] * s), rne_int(o[5] * s), rne_int(o[6] * s), rne_int(o[7] * s));
+    } else {
+      *reinterpret_cast<uint2*>(crow + 8 * ch) =
+          make_uint2(pack4_a8(rne_int(o[0] * s), rne_int(o[1] * s), rne_int(o[2] * s), rne_int(o[3] * s)),
+                     pack4_a8(rne_int(o[4] * s), rne_int(o[5] * s), rne_int(o[6] * s), rne_int(o[7] * s)));
+    }
+  };
+  if constexpr (NCH > 0) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int ch = tid + 256 * c;
+      if (ch < nch) put(ch, v[c]);
+    }
+  } else {
+    for (int ch = tid; ch < nch; ch += 256) {
+      float o[8];
+      load8(ch, o);
+      scale8(ch, o);
+      put(ch, o);
+    }
+  }
+  if (tid == 0) deq[row] = zero ? 0.0f : __fmul_rn(amax / Qb, r);
+}
+
+template <int L, int ABITS, int XT>
+hipError_t launch_h(const void* x, int64_t M, const float* gamma, float eps, int norm, uint8_t* codes, float* deq,
+                    hipStream_t s) {
+  constexpr int K = 1 << L;
+  constexpr int T = K / 64;
+  constexpr int WG = block_threads<L>();
+  constexpr int R = WG / T;
+  const float hK = (float)(1.0 / std::sqrt((double)K));
+  const int64_t blocks = (M + R - 1) / R;
+  hipLaunchKernelGGL((k_actquant_h<L, ABITS, XT>), dim3((unsigned)blocks), dim3(WG), 0, s, x, M, gamma, eps, norm,
+                     hK, codes, deq);
+  return hipGetLastError();
+}
+
+template <int ABITS, int XT>
+hipError_t dispatch_h(int L, const void* x, int64_t M, const float* gamma, float eps, int norm, uint8_t* codes,
+                      float* deq, hipStream_t s) {
+  switch (L) {
+    case 6: return launch_h<6, ABITS, XT>(x, M, gamma, eps, norm, codes, deq, s);
+    case 7: return launch_h<7, ABITS, XT>(x, M, gamma, eps, norm, codes, deq, s);
+    case 8: return launch_h<8, ABITS, XT>(x, M, gamma, eps, norm, codes, deq, s);
+    case 9: return launch_h<9, ABITS, XT>(x, M, gamma, eps, norm, codes, deq, s);
+    case 10: return launch_h<10, ABITS, XT>(x, M, gamma, eps, norm, codes, deq, s);
+    case 11: return launch_h<11, ABITS, XT>(x, M, gamma, eps, norm, codes, deq, s);
+    case 12: return launch_h<12, ABITS, XT>(x, M, gamma, eps, norm, codes, deq, s);
+    case 13: return launch_h<13, ABITS, XT>(x, M, gamma, eps, norm, codes, deq, s);
+    case 14: return launch_h<14, ABITS, XT>(x, M, gamma, eps, norm, codes, deq, s);
+    case 15: return launch_h<15, ABITS, XT>(x, M, gamma, eps, norm, codes, deq, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int ABITS, int XT>
+hipError_t dispatch_plain(const void* x, int64_t M, int64_t K, const float* gamma, float eps, int norm,
+                          uint8_t* codes, float* deq, hipStream_t s) {
+  const int64_t nch = K / 8;
+  const dim3 grid((unsigned)M), block(256);
+  if (nch <= 256)
+    hipLaunchKernelGGL((k_actquant_plain<ABITS, XT, 1>), grid, block, 0, s, x, M, K, gamma, eps, norm, codes, deq);
+  else if (nch <= 512)
+    hipLaunchKernelGGL((k_actquant_plain<ABITS, XT, 2>), grid, block, 0, s, x, M, K, gamma, eps, norm, codes, deq);
+  else if (nch <= 1024)
+    hipLaunchKernelGGL((k_actquant_plain<ABITS, XT, 4>), grid, block, 0, s, x, M, K, gamma, eps, norm, codes, deq);
+  else if (nch <= 2048)
+    hipLaunchKernelGGL((k_actquant_plain<ABITS, XT, 8>), grid, block, 0, s, x, M, K, gamma, eps, norm, codes, deq);
+  else
+    hipLaunchKernelGGL((k_actquant_plain<ABITS, XT, 0>), grid, block, 0, s, x, M, K, gamma, eps, norm, codes, deq);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_actquant(const void* x, int xt, int64_t M, int64_t K, int norm, const float* gamma, float eps,
+                           int abits, int use_h, uint8_t* codes, float* deq, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  if (use_h) {
+    int L = 0;
+    while ((int64_t(1) << L) < K) ++L;
+    if (abits == 4)
+      return xt ? dispatch_h<4, 1>(L, x, M, gamma, eps, norm, codes, deq, s)
+                : dispatch_h<4, 0>(L, x, M, gamma, eps, norm, codes, deq, s);
+    return xt ? dispatch_h<8, 1>(L, x, M, gamma, eps, norm, codes, deq, s)
+              : dispatch_h<8, 0>(L, x, M, gamma, eps, norm, codes, deq, s);
+  }
+  if (abits == 4)
+    return xt ? dispatch_plain<4, 1>(x, M, K, gamma, eps, norm, codes, deq, s)
+              : dispatch_plain<4, 0>(x, M, K, gamma, eps, norm, codes, deq, s);
+  return xt ? dispatch_plain<8, 1>(x, M, K, gamma, eps, norm, codes, deq, s)
+            : dispatch_plain<8, 0>(x, M, K, gamma, eps, norm, codes, deq, s);
+}
+
+}  // namespace hbl

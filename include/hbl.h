@@ -34,7 +34,7 @@
  *                                                          each pair (j, j+h) -> (a+b, a-b) in fp32;
  *                                                          z = H_K u with H_K[i][j] = (-1)^popcount(i&j))
  *      g    = max_k |z_k|
- *      if g == 0:  q = 0 and deq = 0
+ *      if g < 2^-120:  q = 0 and deq = 0          (covers g == 0; keeps Qb/g finite)
  *      else:       s = fl32(Qb / g);  q_k = clamp( rint_ne( fl32(z_k * s) ), -Qb-1, Qb )
  *                  deq = fl32( fl32( fl32(g / Qb) * r ) * hK ),  hK = use_hadamard ? (float)(1/sqrt(K)) : 1
  *  The Hadamard transform is the orthonormal one, H_K / sqrt(K); the 1/sqrt(K) and the

@@ -142,7 +142,8 @@ int orc_quantize_weights(const float* W, int64_t N, int64_t K, int8_t* T, float*
  *   xf = (float)x;  u = norm ? fl32(xf * gamma) : xf
  *   r  = norm ? (float)(1 / sqrt(sum(xf^2 in fp64)/K + eps)) : 1
  *   z  = use_h ? FWHT_fp32(u) : u
- *   g  = max |z|; g == 0 -> q = 0, deq = 0
+ *   g  = max |z|; g < 2^-120 (this covers g == 0) -> q = 0, deq = 0, so that Qb/g
+ *        below stays finite
  *   s  = fl32(Qb / g);  q = clamp(rint(fl32(z * s)), -Qb-1, Qb)
  *   deq = fl32(fl32(fl32(g / Qb) * r) * hK),  hK = use_h ? (float)(1/sqrt(K)) : 1
  *
@@ -186,7 +187,7 @@ int orc_quantize_activations(const void* x, int dtype, int64_t M, int64_t K, int
       float a = fabsf(z[k]);
       if (a > g) g = a;
     }
-    if (g == 0.0f) {
+    if (g < 0x1p-120f) {
       for (int64_t k = 0; k < K; ++k) q[m * K + k] = 0;
       deq[m] = 0.0f;
     } else {
