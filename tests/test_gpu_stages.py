@@ -116,7 +116,7 @@ def test_actquant_plain_bitlinear(orc, K, abits):
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 64, 1), (16, 256, 256), (200, 320, 136), (129, 1024, 257), (300, 2048, 520),
-                                   (64, 16384, 64)])
+                                   (64, 16384, 64), (2500, 576, 2200)])
 @pytest.mark.parametrize("abits", [4, 8])
 def test_gemm_s32_bit_exact(orc, M, K, N, abits):
     note("gemm_s32", M, K, N, abits)
