@@ -47,7 +47,22 @@ def parse():
     p.add_argument("--abits", type=int, default=4)
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time of the CPU baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-mb", type=int, default=0,
+                   help="only run a plain device-to-device copy of this many MiB (3 times) and exit; used to "
+                        "calibrate the FETCH_SIZE / WRITE_SIZE counters")
     return p.parse_args()
+
+
+def copy_calibration(mb: int) -> None:
+    import torch
+
+    n = mb * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"[bench] copied {mb} MiB three times")
 
 
 def act_bytes_per_token(K: int, abits: int, x_bytes: int) -> int:
@@ -62,6 +77,10 @@ def main():
               "the layer shards over tokens with no exchange, so N GPUs would run this same kernel on M/N rows.",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_mb:
+        copy_calibration(args.copy_mb)
+        return
 
     import numpy as np
     import torch

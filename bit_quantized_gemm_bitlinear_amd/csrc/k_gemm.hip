@@ -21,13 +21,13 @@
 // stage's A/B bytes are loaded from HBM into registers while the current stage is
 // multiplied out of LDS (double-buffered, one barrier per stage).  LDS rows are padded so
 // the fragment reads of 16 lanes from 16 rows hit distinct banks.
+#include <type_traits>
+
 #include "hbl_device.h"
 #include "hbl_internal.h"
 
 namespace hbl {
 namespace {
-
-constexpr int BK = 128;
 
 // Block-to-tile order.  Blocks are dispatched round-robin over the 8 XCDs (block b runs on
 // XCD b % 8), and each XCD has its own L2.  The remap gives every XCD a contiguous chunk of
@@ -46,25 +46,38 @@ __device__ __forceinline__ void tile_of_block(int bid, int nblk, int ntm, int nt
   tn = r / gm;
 }
 
-// One block computes a BM x BN tile of y with NWAVE waves laid out WR x WC; each wave owns
-// (BM/WR) x (BN/WC) as 16x16 MFMA tiles.
-template <int ABITS, int BM, int BN, int WR, int WC, int MODE>
+// Operand fragments of one 32-deep k-step for one wave: per 32-row A tile the lane's 16
+// codes (INT4: 8 packed bytes, INT8: 16 bytes) and per 32-column B tile the lane's 16 packed
+// weights (one 32-bit word), straight from LDS.
+template <int ABITS, int TM, int TN>
+struct Frag {
+  typename std::conditional<ABITS == 4, uint2, uint4>::type a[TM];
+  uint32_t b[TN];
+};
+
+// One block computes a BM x BN tile of y with WR x WC waves; each wave owns
+// (BM/WR) x (BN/WC) as 32x32 tiles of v_mfma_i32_32x32x32_i8 (lane l holds row/column l%32
+// and the 16 k-values 16*(l/32) .. +15 of the 32-deep step; result row 8(v/4)+4(l/32)+v%4,
+// column l%32 in accumulator register v).  K advances in stages of BK (BK/32 k-steps).
+template <int ABITS, int BM, int BN, int WR, int WC, int BK, int MODE>
 __global__ __launch_bounds__(64 * WR * WC) void k_gemm(const uint8_t* __restrict__ A, const float* __restrict__ deq,
                                                        const uint8_t* __restrict__ B,
                                                        const float* __restrict__ w_scale, int M, int N, int K,
                                                        int32_t* __restrict__ acc_out, float* __restrict__ y) {
   constexpr int NT = 64 * WR * WC;                  // threads per block
+  constexpr int KS = BK / 32;                       // k-steps per stage
   constexpr int AB = BK * ABITS / 8;                // bytes of one A row per stage
-  constexpr int AS = AB + (ABITS == 4 ? 8 : 16);    // padded LDS row stride of A
+  constexpr int AS = AB + (ABITS == 4 ? 8 : 16);    // padded LDS row stride of A (b64 / b128 reads)
   constexpr int BB = BK / 4;                        // bytes of one B row per stage
-  constexpr int BS = BB + 8;                        // padded LDS row stride of B
+  constexpr int BS = BB + 4;                        // odd dword stride: 32 lanes, 32 banks
   constexpr int WM = BM / WR, WN = BN / WC;
-  constexpr int TM = WM / 16, TN = WN / 16;
+  constexpr int TM = WM / 32, TN = WN / 32;
   constexpr int ACH = AB / 16;                      // 16-byte chunks per A row per stage
   constexpr int BCH = BB / 16;
   constexpr int ALD = BM * ACH / NT;                // 16-byte loads per thread per stage
   constexpr int BLD = BN * BCH / NT;
   constexpr int SHIFT = ABITS == 4 ? 10 : 6;
+  static_assert(KS % 2 == 0, "stages hold an even number of k-steps");
   static_assert(ALD >= 1 && BLD >= 1 && ALD * NT == BM * ACH && BLD * NT == BN * BCH, "tile/thread mismatch");
 
   __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * AS];
@@ -81,32 +94,48 @@ __global__ __launch_bounds__(64 * WR * WC) void k_gemm(const uint8_t* __restrict
   const int64_t arow = (int64_t)K * ABITS / 8;
   const int64_t brow = K / 4;
   const int KT = (K + BK - 1) / BK;
-  const bool last_half = (K % BK) != 0;
+  const int last_k64 = (K - (KT - 1) * BK) / 64;   // 64-deep slices in the last stage
+
+  // Per-thread global sources, 32-bit offsets from the tile's first row.  Rows past M
+  // (columns past N) are clamped to the last valid one: their products land in accumulator
+  // rows (columns) the epilogue never stores.
+  const uint8_t* Ablk = A + (int64_t)m0 * arow;
+  const uint8_t* Bblk = B + (int64_t)n0 * brow;
+  uint32_t aoff[ALD];
+#pragma unroll
+  for (int i = 0; i < ALD; ++i) {
+    const int e = tid + NT * i, r = e / ACH, c = e % ACH;
+    aoff[i] = (uint32_t)(min(r, M - 1 - m0) * arow + 16 * c);
+  }
+  uint32_t boff[BLD];
+#pragma unroll
+  for (int i = 0; i < BLD; ++i) {
+    const int e = tid + NT * i, r = e / BCH, c = e % BCH;
+    boff[i] = (uint32_t)(min(r, N - 1 - n0) * brow + 16 * c);
+  }
 
   uint4 ra[ALD], rb[BLD];
-  auto gload = [&](int kt, bool half) {
+  // Load stage kt.  In the last stage only its first n64 64-deep slices exist; the rest of
+  // the stage is zero-filled (zero weights contribute nothing).
+  auto gload = [&](int kt, int n64) {
+    const int va = n64 * 64 * ABITS / 8 / 16, vb = n64;
+    const bool full = n64 * 64 == BK;
+    const uint8_t* ak = Ablk + (int64_t)kt * AB;
+    const uint8_t* bk = Bblk + (int64_t)kt * BB;
 #pragma unroll
-    for (int i = 0; i < ALD; ++i) {
-      const int e = tid + NT * i, r = e / ACH, c = e % ACH;
-      const int gm = m0 + r;
-      const bool ok = gm < M && (!half || c < ACH / 2);
-      ra[i] = ok ? *reinterpret_cast<const uint4*>(A + (int64_t)gm * arow + (int64_t)kt * AB + 16 * c)
-                 : make_uint4(0, 0, 0, 0);
-    }
+    for (int i = 0; i < ALD; ++i)
+      ra[i] = (full || (int)((tid + NT * i) % ACH) < va) ? *reinterpret_cast<const uint4*>(ak + aoff[i])
+                                                          : make_uint4(0, 0, 0, 0);
 #pragma unroll
-    for (int i = 0; i < BLD; ++i) {
-      const int e = tid + NT * i, r = e / BCH, c = e % BCH;
-      const int gn = n0 + r;
-      const bool ok = gn < N && (!half || c < BCH / 2);
-      rb[i] = ok ? *reinterpret_cast<const uint4*>(B + (int64_t)gn * brow + (int64_t)kt * BB + 16 * c)
-                 : make_uint4(0, 0, 0, 0);
-    }
+    for (int i = 0; i < BLD; ++i)
+      rb[i] = (full || (int)((tid + NT * i) % BCH) < vb) ? *reinterpret_cast<const uint4*>(bk + boff[i])
+                                                          : make_uint4(0, 0, 0, 0);
   };
   auto swrite = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < ALD; ++i) {
-      const int e = tid + NT * i, r = e / ACH, c = e % ACH;
-      uint8_t* d = &sA[buf][r * AS + 16 * c];
+      const int e = tid + NT * i;
+      uint8_t* d = &sA[buf][(e / ACH) * AS + 16 * (e % ACH)];
       if constexpr (ABITS == 8) {
         *reinterpret_cast<uint4*>(d) = ra[i];
       } else {
@@ -116,56 +145,80 @@ __global__ __launch_bounds__(64 * WR * WC) void k_gemm(const uint8_t* __restrict
     }
 #pragma unroll
     for (int i = 0; i < BLD; ++i) {
-      const int e = tid + NT * i, r = e / BCH, c = e % BCH;
-      uint8_t* d = &sB[buf][r * BS + 16 * c];
-      reinterpret_cast<uint2*>(d)[0] = make_uint2(rb[i].x, rb[i].y);
-      reinterpret_cast<uint2*>(d)[1] = make_uint2(rb[i].z, rb[i].w);
+      const int e = tid + NT * i;
+      uint32_t* d = reinterpret_cast<uint32_t*>(&sB[buf][(e / BCH) * BS + 16 * (e % BCH)]);
+      d[0] = rb[i].x;
+      d[1] = rb[i].y;
+      d[2] = rb[i].z;
+      d[3] = rb[i].w;
     }
   };
 
-  v4i acc[TM][TN];
+  using F = Frag<ABITS, TM, TN>;
+  constexpr int AKS = ABITS == 4 ? 16 : 32;         // A bytes per row per 32-deep step
+  const int arow0 = (wm * WM + (lane & 31)) * AS + (AKS / 2) * (lane >> 5);
+  const int brow0 = (wn * WN + (lane & 31)) * BS + 4 * (lane >> 5);
+  auto fread = [&](int buf, int ks, F& f) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const uint8_t* p = &sA[buf][arow0 + 32 * i * AS + ks * AKS];
+      if constexpr (ABITS == 4) f.a[i] = *reinterpret_cast<const uint2*>(p);
+      else f.a[i] = *reinterpret_cast<const uint4*>(p);
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) f.b[j] = *reinterpret_cast<const uint32_t*>(&sB[buf][brow0 + 32 * j * BS + ks * 8]);
+  };
+
+  v16i acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+    for (int j = 0; j < TN; ++j) acc[i][j] = v16i{};
 
-  auto compute_step = [&](int buf, int ks) {
+  auto fmma = [&](const F& f) {
     v4i b[TN];
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      const int r = wn * WN + 16 * j + (lane & 15);
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(&sB[buf][r * BS + ks * 16 + 4 * (lane >> 4)]);
+      const uint32_t w = f.b[j];
       b[j] = v4i{(int)((w << 6) & 0xC0C0C0C0u), (int)((w << 4) & 0xC0C0C0C0u), (int)((w << 2) & 0xC0C0C0C0u),
                  (int)(w & 0xC0C0C0C0u)};
     }
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       v4i a;
-      const int r = wm * WM + 16 * i + (lane & 15);
       if constexpr (ABITS == 4) {
-        const uint2 w = *reinterpret_cast<const uint2*>(&sA[buf][r * AS + ks * 32 + 8 * (lane >> 4)]);
+        const uint2 w = f.a[i];
         a = v4i{(int)((w.x << 4) & 0xF0F0F0F0u), (int)(w.x & 0xF0F0F0F0u), (int)((w.y << 4) & 0xF0F0F0F0u),
                 (int)(w.y & 0xF0F0F0F0u)};
       } else {
-        const uint4 w = *reinterpret_cast<const uint4*>(&sA[buf][r * AS + ks * 64 + 16 * (lane >> 4)]);
+        const uint4 w = f.a[i];
         a = v4i{(int)w.x, (int)w.y, (int)w.z, (int)w.w};
       }
 #pragma unroll
-      for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b[j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b[j], acc[i][j], 0, 0, 0);
     }
   };
 
-  gload(0, KT == 1 && last_half);
+  F f0, f1;
+  gload(0, KT == 1 ? last_k64 : BK / 64);
   swrite(0);
   __syncthreads();
+  fread(0, 0, f0);
   for (int kt = 0; kt < KT; ++kt) {
-    const bool has_next = kt + 1 < KT;
-    if (has_next) gload(kt + 1, kt + 1 == KT - 1 && last_half);
     const int buf = kt & 1;
-    compute_step(buf, 0);
-    if (!(kt == KT - 1 && last_half)) compute_step(buf, 1);
+    const bool has_next = kt + 1 < KT;
+    if (has_next) gload(kt + 1, kt + 1 == KT - 1 ? last_k64 : BK / 64);
+    // k-steps ping-pong between two fragment sets, each read one step ahead.
+#pragma unroll
+    for (int ks = 0; ks < KS; ks += 2) {
+      fread(buf, ks + 1, f1);
+      fmma(f0);
+      if (ks + 2 < KS) fread(buf, ks + 2, f0);
+      fmma(f1);
+    }
     if (has_next) swrite(buf ^ 1);
     __syncthreads();
+    if (has_next) fread(buf ^ 1, 0, f0);
   }
 
   float alpha = 0.0f;
@@ -173,14 +226,14 @@ __global__ __launch_bounds__(64 * WR * WC) void k_gemm(const uint8_t* __restrict
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int m = m0 + wm * WM + 16 * i + 4 * (lane >> 4) + v;
+    for (int v = 0; v < 16; ++v) {
+      const int m = m0 + wm * WM + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
       if (m >= M) continue;
       float dm = 0.0f;
       if constexpr (MODE == 1) dm = deq[m];
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const int n = n0 + wn * WN + 16 * j + (lane & 15);
+        const int n = n0 + wn * WN + 32 * j + (lane & 31);
         if (n >= N) continue;
         const int val = acc[i][j][v] >> SHIFT;
         if constexpr (MODE == 0) {
@@ -193,11 +246,11 @@ __global__ __launch_bounds__(64 * WR * WC) void k_gemm(const uint8_t* __restrict
   }
 }
 
-template <int ABITS, int BM, int BN, int WR, int WC, int MODE>
+template <int ABITS, int BM, int BN, int WR, int WC, int BK, int MODE>
 hipError_t launch_cfg(const uint8_t* codes, const float* deq, const uint8_t* Wq, const float* w_scale, int64_t M,
                       int64_t K, int64_t N, int32_t* acc, float* y, hipStream_t s) {
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  hipLaunchKernelGGL((k_gemm<ABITS, BM, BN, WR, WC, MODE>), dim3((unsigned)tiles), dim3(64 * WR * WC), 0, s, codes,
+  hipLaunchKernelGGL((k_gemm<ABITS, BM, BN, WR, WC, BK, MODE>), dim3((unsigned)tiles), dim3(64 * WR * WC), 0, s, codes,
                      deq, Wq, w_scale, (int)M, (int)N, (int)K, acc, y);
   return hipGetLastError();
 }
@@ -216,9 +269,10 @@ inline bool use_big_tiles(int64_t M, int64_t N) {
 template <int ABITS, int MODE>
 hipError_t launch(const uint8_t* codes, const float* deq, const uint8_t* Wq, const float* w_scale, int64_t M,
                   int64_t K, int64_t N, int32_t* acc, float* y, hipStream_t s) {
+  constexpr int BKBIG = ABITS == 4 ? 256 : 128;  // INT8 A tiles are twice as wide in LDS
   if (use_big_tiles(M, N))
-    return launch_cfg<ABITS, 256, 256, 2, 4, MODE>(codes, deq, Wq, w_scale, M, K, N, acc, y, s);
-  return launch_cfg<ABITS, 128, 128, 2, 2, MODE>(codes, deq, Wq, w_scale, M, K, N, acc, y, s);
+    return launch_cfg<ABITS, 256, 256, 2, 4, BKBIG, MODE>(codes, deq, Wq, w_scale, M, K, N, acc, y, s);
+  return launch_cfg<ABITS, 128, 128, 2, 2, 128, MODE>(codes, deq, Wq, w_scale, M, K, N, acc, y, s);
 }
 
 }  // namespace
