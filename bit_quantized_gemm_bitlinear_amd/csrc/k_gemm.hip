@@ -16,11 +16,16 @@
 // The int32 sum is therefore 1024*acc (INT4) or 64*acc (INT8); |acc| <= 127*K keeps it
 // below 2^31 for K <= 2^17 and the final arithmetic shift is exact.
 //
-// Tiling: a 256-thread block computes a BM x BN tile of y; its four waves each own a
-// (BM/2) x (BN/2) sub-tile of 16x16 MFMA tiles.  K advances in stages of 128: the next
-// stage's A/B bytes are loaded from HBM into registers while the current stage is
-// multiplied out of LDS (double-buffered, one barrier per stage).  LDS rows are padded so
-// the fragment reads of 16 lanes from 16 rows hit distinct banks.
+// Tiling for large problems: a 512-thread block computes a 256 x 256 tile of y; its eight
+// waves (2 x 4) each own a 128 x 64 sub-tile of 32x32 MFMA tiles (128 int32 accumulators
+// per lane, two waves per SIMD).  On gfx950 every VALU instruction issued beside an MFMA
+// costs issue time, so the 32x32x32 shape (twice the work per instruction of 16x16x64)
+// and a wide wave tile (each decoded fragment feeds 2-4 MFMAs) keep the decode overhead
+// low.  K advances in LDS stages (256 deep for INT4, 128 for INT8): the next stage is
+// loaded from HBM into registers while the current one is multiplied out of LDS (double
+// buffered, one barrier per stage), and each 32-deep step's fragments are read from LDS
+// one step ahead.  LDS rows are padded so the fragment reads hit distinct banks.  Small
+// problems use 128 x 128 tiles (4 waves) so that more CUs get work.
 #include <type_traits>
 
 #include "hbl_device.h"
@@ -116,21 +121,19 @@ __global__ __launch_bounds__(64 * WR * WC) void k_gemm(const uint8_t* __restrict
 
   uint4 ra[ALD], rb[BLD];
   // Load stage kt.  In the last stage only its first n64 64-deep slices exist; the rest of
-  // the stage is zero-filled (zero weights contribute nothing).
+  // the stage is zero-filled (zero weights and codes contribute nothing).
   auto gload = [&](int kt, int n64) {
     const int va = n64 * 64 * ABITS / 8 / 16, vb = n64;
-    const bool full = n64 * 64 == BK;
     const uint8_t* ak = Ablk + (int64_t)kt * AB;
     const uint8_t* bk = Bblk + (int64_t)kt * BB;
 #pragma unroll
     for (int i = 0; i < ALD; ++i)
-      ra[i] = (full || (int)((tid + NT * i) % ACH) < va) ? *reinterpret_cast<const uint4*>(ak + aoff[i])
-                                                          : make_uint4(0, 0, 0, 0);
+      ra[i] = (int)((tid + NT * i) % ACH) < va ? *reinterpret_cast<const uint4*>(ak + aoff[i]) : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int i = 0; i < BLD; ++i)
-      rb[i] = (full || (int)((tid + NT * i) % BCH) < vb) ? *reinterpret_cast<const uint4*>(bk + boff[i])
-                                                          : make_uint4(0, 0, 0, 0);
+      rb[i] = (int)((tid + NT * i) % BCH) < vb ? *reinterpret_cast<const uint4*>(bk + boff[i]) : make_uint4(0, 0, 0, 0);
   };
+  auto load_stage = [&](int kt) { gload(kt, kt == KT - 1 ? last_k64 : BK / 64); };
   auto swrite = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < ALD; ++i) {
@@ -200,14 +203,14 @@ __global__ __launch_bounds__(64 * WR * WC) void k_gemm(const uint8_t* __restrict
   };
 
   F f0, f1;
-  gload(0, KT == 1 ? last_k64 : BK / 64);
+  load_stage(0);
   swrite(0);
   __syncthreads();
   fread(0, 0, f0);
   for (int kt = 0; kt < KT; ++kt) {
     const int buf = kt & 1;
     const bool has_next = kt + 1 < KT;
-    if (has_next) gload(kt + 1, kt + 1 == KT - 1 ? last_k64 : BK / 64);
+    if (has_next) load_stage(kt + 1);
     // k-steps ping-pong between two fragment sets, each read one step ahead.
 #pragma unroll
     for (int ks = 0; ks < KS; ks += 2) {
