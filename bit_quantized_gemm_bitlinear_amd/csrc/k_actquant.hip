@@ -136,24 +136,46 @@ __device__ __forceinline__ void store_words(uint8_t* dst, const uint32_t* w) {
   }
 }
 
-// Quantise a run of RL consecutive row elements v[0 .. RL) starting at row element k0 and
-// store its packed bytes (INT4: 8 codes per word at byte k0/2; INT8: 4 codes per word).
+// Round-half-even to an integer through the fp32 adder: for |v| <= 2^21, v + (1.5*2^23 + c)
+// rounds to the integer rint(v) + c (spacing 1 in [2^23, 2^24), ties to even; c even keeps
+// the parity), whose low mantissa bits are then rint(v) + c in two's complement.
+__device__ __forceinline__ uint32_t rne_bits(float v, float magic) { return __float_as_uint(v + magic); }
+
+// Quantise a run of RL consecutive row elements v[0 .. RL) (scale s) starting at row
+// element k0 and store its packed bytes.
+//  INT4: offset magic +8 gives low nibble q+8 in [1,15] with zero bits above it, so a pair
+//        (lo, hi) becomes one byte with a single shift-or; four bytes are gathered with
+//        v_perm and the offset is removed with one xor (q+8 ^ 8 = q mod 16).
+//  INT8: the low byte of the rounded value is q mod 256; four are gathered with v_perm.
 template <int ABITS, int RL>
 __device__ __forceinline__ void store_run(const float* v, float s, uint8_t* __restrict__ crow, int k0) {
+  constexpr float MAGIC = 12582912.0f;  // 1.5 * 2^23
   if constexpr (ABITS == 4) {
     uint32_t w[RL / 8];
 #pragma unroll
-    for (int d = 0; d < RL / 8; ++d)
-      w[d] = pack8_a4(rne_int(v[8 * d + 0] * s), rne_int(v[8 * d + 1] * s), rne_int(v[8 * d + 2] * s),
-                      rne_int(v[8 * d + 3] * s), rne_int(v[8 * d + 4] * s), rne_int(v[8 * d + 5] * s),
-                      rne_int(v[8 * d + 6] * s), rne_int(v[8 * d + 7] * s));
+    for (int d = 0; d < RL / 8; ++d) {
+      uint32_t b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = rne_bits(v[8 * d + i] * s, MAGIC + 8.0f);
+        const uint32_t hi = rne_bits(v[8 * d + i + 4] * s, MAGIC + 8.0f);
+        b[i] = (hi << 4) | lo;  // byte 0 = (hi+8) << 4 | (lo+8); higher bytes unused
+      }
+      const uint32_t b01 = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u);
+      const uint32_t b23 = __builtin_amdgcn_perm(b[3], b[2], 0x04000c0cu);
+      w[d] = (b01 | b23) ^ 0x88888888u;
+    }
     store_words<RL / 8>(crow + k0 / 2, w);
   } else {
     uint32_t w[RL / 4];
 #pragma unroll
-    for (int d = 0; d < RL / 4; ++d)
-      w[d] = pack4_a8(rne_int(v[4 * d + 0] * s), rne_int(v[4 * d + 1] * s), rne_int(v[4 * d + 2] * s),
-                      rne_int(v[4 * d + 3] * s));
+    for (int d = 0; d < RL / 4; ++d) {
+      const uint32_t q0 = rne_bits(v[4 * d + 0] * s, MAGIC), q1 = rne_bits(v[4 * d + 1] * s, MAGIC);
+      const uint32_t q2 = rne_bits(v[4 * d + 2] * s, MAGIC), q3 = rne_bits(v[4 * d + 3] * s, MAGIC);
+      const uint32_t lo = __builtin_amdgcn_perm(q1, q0, 0x0c0c0400u);
+      const uint32_t hi = __builtin_amdgcn_perm(q3, q2, 0x04000c0cu);
+      w[d] = lo | hi;
+    }
     store_words<RL / 4>(crow + k0, w);
   }
 }
@@ -179,9 +201,48 @@ constexpr int block_threads() {
   return (1 << L) / 64 > 256 ? (1 << L) / 64 : 256;
 }
 
-template <int L, int ABITS, int XT>
+// Raw input of one thread's 64 consecutive row elements (bf16: 8 x 16 bytes, fp32: 16 x 16).
+template <int XT>
+struct RowChunk {
+  uint4 w[XT == 1 ? 8 : 16];
+};
+
+template <int XT>
+__device__ __forceinline__ void load_chunk(RowChunk<XT>& c, const void* x, int64_t elem0) {
+  const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(x) + elem0 * (XT == 1 ? 2 : 4));
+#pragma unroll
+  for (int i = 0; i < (XT == 1 ? 8 : 16); ++i) c.w[i] = src[i];
+}
+
+template <int XT>
+__device__ __forceinline__ void unpack_chunk(const RowChunk<XT>& c, float (&v)[64]) {
+#pragma unroll
+  for (int i = 0; i < (XT == 1 ? 8 : 16); ++i) {
+    const uint4 w = c.w[i];
+    if constexpr (XT == 1) {
+      v[8 * i + 0] = bf16lo(w.x);
+      v[8 * i + 1] = bf16hi(w.x);
+      v[8 * i + 2] = bf16lo(w.y);
+      v[8 * i + 3] = bf16hi(w.y);
+      v[8 * i + 4] = bf16lo(w.z);
+      v[8 * i + 5] = bf16hi(w.z);
+      v[8 * i + 6] = bf16lo(w.w);
+      v[8 * i + 7] = bf16hi(w.w);
+    } else {
+      v[4 * i + 0] = __uint_as_float(w.x);
+      v[4 * i + 1] = __uint_as_float(w.y);
+      v[4 * i + 2] = __uint_as_float(w.z);
+      v[4 * i + 3] = __uint_as_float(w.w);
+    }
+  }
+}
+
+// NM: 0 = no norm, 1 = RMSNorm with unit gamma, 2 = RMSNorm with gamma.
+// Blocks are persistent: block b handles row groups b, b + gridDim.x, ...; the raw input of
+// the next group is loaded into registers while the current one is transformed.
+template <int L, int ABITS, int XT, int NM>
 __global__ __launch_bounds__(block_threads<L>()) void k_actquant_h(
-    const void* __restrict__ x, int64_t M, const float* __restrict__ gamma, float eps, int norm, float hK,
+    const void* __restrict__ x, int64_t M, const float* __restrict__ gamma, float eps, float hK,
     uint8_t* __restrict__ codes, float* __restrict__ deq) {
   constexpr int K = 1 << L;
   constexpr int T = K / 64;           // threads per row
@@ -190,6 +251,7 @@ __global__ __launch_bounds__(block_threads<L>()) void k_actquant_h(
   constexpr int NP = nphases(L);
   constexpr int ROWF = K + K / 16;    // padded floats per LDS row
   constexpr int NW = WG / 64;
+  constexpr float Qb = QB<ABITS>::value;
   __shared__ float lds[NP > 1 ? R * ROWF : 1];
   __shared__ float redf[NW];
   __shared__ double redd[NW];
@@ -197,101 +259,83 @@ __global__ __launch_bounds__(block_threads<L>()) void k_actquant_h(
   const int tid = threadIdx.x;
   const int rl = tid / T;
   const int t = tid % T;
-  const int64_t row = (int64_t)blockIdx.x * R + rl;
-  const bool valid = row < M;
-
-  float v[64];
-  if (valid) {
-    if constexpr (XT == 1) {
-      const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + row * K + 64 * t);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        uint4 w = src[i];
-        v[8 * i + 0] = bf16lo(w.x);
-        v[8 * i + 1] = bf16hi(w.x);
-        v[8 * i + 2] = bf16lo(w.y);
-        v[8 * i + 3] = bf16hi(w.y);
-        v[8 * i + 4] = bf16lo(w.z);
-        v[8 * i + 5] = bf16hi(w.z);
-        v[8 * i + 6] = bf16lo(w.w);
-        v[8 * i + 7] = bf16hi(w.w);
-      }
-    } else {
-      const float4* src = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + row * K + 64 * t);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float4 f = src[i];
-        v[4 * i + 0] = f.x;
-        v[4 * i + 1] = f.y;
-        v[4 * i + 2] = f.z;
-        v[4 * i + 3] = f.w;
-      }
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < 64; ++j) v[j] = 0.0f;
-  }
-
-  float r = 1.0f;
-  if (norm) {
-    double ss = 0.0;
-#pragma unroll
-    for (int j = 0; j < 64; ++j) ss = __builtin_fma((double)v[j], (double)v[j], ss);  // x^2 is exact in fp64
-    ss = row_sum<T>(ss, redd);
-    r = (float)(1.0 / sqrt(ss / (double)K + (double)eps));
-    if (gamma != nullptr) {
-      const float4* gp = reinterpret_cast<const float4*>(gamma + 64 * t);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float4 g = gp[i];
-        v[4 * i + 0] *= g.x;
-        v[4 * i + 1] *= g.y;
-        v[4 * i + 2] *= g.z;
-        v[4 * i + 3] *= g.w;
-      }
-    }
-  }
-
-  // Phase 0: index bits 0..5 in registers.
-  stages<0, phase_desc(L, 0).a>(v);
+  const int64_t ngroups = (M + R - 1) / R;
   float* rowlds = lds + rl * ROWF;
-  if constexpr (NP > 1) {
-    lds_write<L, 0, ROWF>(v, rowlds, t);
-    __syncthreads();
-    lds_read<L, 1, ROWF>(v, rowlds, t);
-    stages<Layout<L, 1>::c, Layout<L, 1>::a>(v);
-  }
-  if constexpr (NP > 2) {
-    lds_write<L, 1, ROWF>(v, rowlds, t);
-    __syncthreads();
-    lds_read<L, 2, ROWF>(v, rowlds, t);
-    stages<Layout<L, 2>::c, Layout<L, 2>::a>(v);
+
+  float g[64];
+  if constexpr (NM == 2) {
+    const float4* gp = reinterpret_cast<const float4*>(gamma + 64 * t);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float4 q = gp[i];
+      g[4 * i + 0] = q.x;
+      g[4 * i + 1] = q.y;
+      g[4 * i + 2] = q.z;
+      g[4 * i + 3] = q.w;
+    }
   }
 
-  float amax = 0.0f;
-#pragma unroll
-  for (int j = 0; j < 64; ++j) amax = fmaxf(amax, fabsf(v[j]));
-  amax = row_max<T>(amax, redf);
+  RowChunk<XT> cur, nxt;
+  int64_t grp = blockIdx.x;
+  if (grp < ngroups) load_chunk<XT>(cur, x, min(grp * R + rl, M - 1) * K + 64 * t);
+  for (; grp < ngroups; grp += gridDim.x) {
+    const int64_t row = grp * R + rl;
+    const bool valid = row < M;        // rows past M are computed from row M-1, never stored
+    const int64_t ngrp = grp + gridDim.x;
+    if (ngrp < ngroups) load_chunk<XT>(nxt, x, min(ngrp * R + rl, M - 1) * K + 64 * t);
 
-  if (!valid) return;
-  constexpr float Qb = QB<ABITS>::value;
-  uint8_t* crow = codes + row * (int64_t)(K * ABITS / 8);
-  constexpr int LASTP = NP - 1;
-  using LY = Layout<L, LASTP>;
-  constexpr int RL = NP == 1 ? 64 : (1 << LY::c);  // run of consecutive elements in registers
-  const int b = NP == 1 ? 0 : LY::base(t);
-  float dq = 0.0f;
-  if (amax < 0x1p-120f) {
-    const float zero[64] = {};
+    float v[64];
+    unpack_chunk<XT>(cur, v);
+    float r = 1.0f;
+    if constexpr (NM != 0) {
+      double ss = 0.0;
 #pragma unroll
-    for (int g = 0; g < 64 / RL; ++g) store_run<ABITS, RL>(zero + g * RL, 0.0f, crow, NP == 1 ? 64 * t : b + LY::off(g * RL));
-  } else {
-    const float s = Qb / amax;
+      for (int j = 0; j < 64; ++j) ss = __builtin_fma((double)v[j], (double)v[j], ss);  // x^2 exact in fp64
+      ss = row_sum<T>(ss, redd);
+      r = (float)(1.0 / sqrt(ss / (double)K + (double)eps));
+      if constexpr (NM == 2) {
 #pragma unroll
-    for (int g = 0; g < 64 / RL; ++g) store_run<ABITS, RL>(v + g * RL, s, crow, NP == 1 ? 64 * t : b + LY::off(g * RL));
-    dq = __fmul_rn(__fmul_rn(amax / Qb, r), hK);
+        for (int j = 0; j < 64; ++j) v[j] *= g[j];
+      }
+    }
+
+    // Phase 0: index bits 0..5 in registers.
+    stages<0, phase_desc(L, 0).a>(v);
+    if constexpr (NP > 1) {
+      lds_write<L, 0, ROWF>(v, rowlds, t);
+      __syncthreads();
+      lds_read<L, 1, ROWF>(v, rowlds, t);
+      stages<Layout<L, 1>::c, Layout<L, 1>::a>(v);
+    }
+    if constexpr (NP > 2) {
+      lds_write<L, 1, ROWF>(v, rowlds, t);
+      __syncthreads();
+      lds_read<L, 2, ROWF>(v, rowlds, t);
+      stages<Layout<L, 2>::c, Layout<L, 2>::a>(v);
+    }
+
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 64; ++j) amax = fmaxf(amax, fabsf(v[j]));
+    amax = row_max<T>(amax, redf);
+
+    const bool zero = amax < 0x1p-120f;     // also keeps Qb / amax finite
+    const float s = zero ? 0.0f : Qb / amax;  // s = 0 quantises the whole row to 0
+    if (valid) {
+      uint8_t* crow = codes + row * (int64_t)(K * ABITS / 8);
+      constexpr int LASTP = NP - 1;
+      using LY = Layout<L, LASTP>;
+      constexpr int RL = NP == 1 ? 64 : (1 << LY::c);  // run of consecutive elements in registers
+      const int b = NP == 1 ? 64 * t : LY::base(t);
+#pragma unroll
+      for (int gi = 0; gi < 64 / RL; ++gi)
+        store_run<ABITS, RL>(v + gi * RL, s, crow, NP == 1 ? b + gi * RL : b + LY::off(gi * RL));
+      if (t == 0) deq[row] = zero ? 0.0f : __fmul_rn(__fmul_rn(amax / Qb, r), hK);
+    }
+    cur = nxt;
+    // The next group reuses LDS and the reduction slots: every thread must be done with them.
+    __syncthreads();
   }
-  if (t == 0) deq[row] = dq;
 }
 
 // BitLinear path (no transform), any K with K % 64 == 0: one 256-thread block per row,
@@ -402,9 +446,16 @@ hipError_t launch_h(const void* x, int64_t M, const float* gamma, float eps, int
   constexpr int WG = block_threads<L>();
   constexpr int R = WG / T;
   const float hK = (float)(1.0 / std::sqrt((double)K));
-  const int64_t blocks = (M + R - 1) / R;
-  hipLaunchKernelGGL((k_actquant_h<L, ABITS, XT>), dim3((unsigned)blocks), dim3(WG), 0, s, x, M, gamma, eps, norm,
-                     hK, codes, deq);
+  const int64_t groups = (M + R - 1) / R;
+  // Persistent blocks: two resident per CU (LDS-limited) on 256 CUs, a few rounds deep.
+  const int64_t blocks = groups < 2048 ? groups : 2048;
+  const dim3 grid((unsigned)blocks), block(WG);
+  if (!norm)
+    hipLaunchKernelGGL((k_actquant_h<L, ABITS, XT, 0>), grid, block, 0, s, x, M, gamma, eps, hK, codes, deq);
+  else if (gamma == nullptr)
+    hipLaunchKernelGGL((k_actquant_h<L, ABITS, XT, 1>), grid, block, 0, s, x, M, gamma, eps, hK, codes, deq);
+  else
+    hipLaunchKernelGGL((k_actquant_h<L, ABITS, XT, 2>), grid, block, 0, s, x, M, gamma, eps, hK, codes, deq);
   return hipGetLastError();
 }
 
