@@ -90,7 +90,7 @@ def main():
 
     wl = inputs.WORKLOADS[args.workload]
     if wl.name == "ffn_7b":
-        raise SystemExit("use bench_ffn (not part of the headline); --workload must be a single layer")
+        return bench_ffn(args, wl)
     abits = args.abits
     M, K, N = wl.M, wl.K, wl.N
     dev = torch.device("cuda:0")
@@ -225,6 +225,93 @@ def main():
                                              "(read x, write packed codes + deq)"},
         "cpu_baseline": cpu,
     }
+    print(json.dumps(out), flush=True)
+
+
+def bench_ffn(args, wl):
+    """The 7B-like a4 FFN block: RMSNorm -> INT4 BitLinear gate and up (one shared activation
+    quantisation) -> SwiGLU -> H-BitLinear down.  Reported separately from the headline."""
+    import numpy as np
+    import torch
+
+    from bit_quantized_gemm_bitlinear_amd import binding as B
+    from bit_quantized_gemm_bitlinear_amd import inputs
+
+    M, hid, ffn = wl.M, wl.extra["hidden"], wl.extra["ffn"]
+    dev = torch.device("cuda:0")
+    log(f"[bench] workload {wl.name}: M={M} hidden={hid} ffn={ffn}")
+    x_np = wl.activations()
+    x = torch.from_numpy(x_np.view(np.int16)).to(dev).view(torch.bfloat16)
+    Wq = {}
+    for name, (n, k, seed) in {"gate": (ffn, hid, wl.extra["seed_gate"]), "up": (ffn, hid, wl.extra["seed_up"]),
+                               "down": (hid, ffn, wl.extra["seed_down"])}.items():
+        Wq[name] = B.quantize_weights(torch.from_numpy(inputs.make_weights(n, k, seed=seed)).to(dev))
+    torch.cuda.synchronize()
+    L = B.lib()
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    codes = torch.empty((M, hid // 2), dtype=torch.uint8, device=dev)
+    deq = torch.empty(M, dtype=torch.float32, device=dev)
+    g = torch.empty((M, ffn), dtype=torch.float32, device=dev)
+    u = torch.empty_like(g)
+    h = torch.empty_like(g)
+    y = torch.empty((M, hid), dtype=torch.float32, device=dev)
+    ws = B.forward_workspace(M, ffn, 4, dev)
+
+    def ok(st):
+        if st != 0:
+            raise RuntimeError(L.hbl_last_error().decode())
+
+    def q():
+        ok(L.hbl_quantize_activations(x.data_ptr(), B.HBL_BF16, M, hid, B.HBL_NORM_RMS, None, 1e-5, 4, 0,
+                                      codes.data_ptr(), deq.data_ptr(), sh))
+
+    def gate():
+        ok(L.hbl_gemm_dequant(codes.data_ptr(), deq.data_ptr(), Wq["gate"][0].data_ptr(), Wq["gate"][1].data_ptr(),
+                              M, hid, ffn, 4, g.data_ptr(), sh))
+
+    def up():
+        ok(L.hbl_gemm_dequant(codes.data_ptr(), deq.data_ptr(), Wq["up"][0].data_ptr(), Wq["up"][1].data_ptr(),
+                              M, hid, ffn, 4, u.data_ptr(), sh))
+
+    def glu():
+        ok(L.hbl_swiglu(g.data_ptr(), u.data_ptr(), g.numel(), h.data_ptr(), sh))
+
+    def down():
+        ok(L.hbl_forward(h.data_ptr(), B.HBL_F32, Wq["down"][0].data_ptr(), Wq["down"][1].data_ptr(), M, ffn, hid, 4,
+                         1, B.HBL_NORM_RMS, None, 1e-5, y.data_ptr(), ws.data_ptr(), ws.numel(), sh))
+
+    parts = [("actquant_gate_up", q), ("gemm_gate", gate), ("gemm_up", up), ("swiglu", glu), ("down_forward", down)]
+    for _ in range(args.warmup):
+        for _, f in parts:
+            f()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for _, f in parts:
+            f()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)]
+    sums = [0.0] * len(parts)
+    for _ in range(args.steps):
+        ev[0].record(stream)
+        for i, (_, f) in enumerate(parts):
+            f()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        for i in range(len(parts)):
+            sums[i] += ev[i].elapsed_time(ev[i + 1]) * 1e3 / args.steps
+    ops = 3 * 2.0 * M * hid * ffn
+    out = {"metric": "7B-like a4 FFN block tokens/s (RMSNorm, BitLinear gate/up, SwiGLU, H-BitLinear down)",
+           "value": M * args.steps / el, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": el * 1e3 / args.steps, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "i8", "data": "synthetic",
+           "config": {"workload": f"{wl.name}: {wl.description}", "M": M, "hidden": hid, "ffn": ffn, "abits": 4},
+           "effective_tops": ops / (el / args.steps) / 1e12,
+           "parts_us": {name: v for (name, _), v in zip(parts, sums)}}
+    log(f"[bench] ffn block {out['ms_per_step']:.3f} ms/step, parts " +
+        ", ".join(f"{k} {v:.0f} us" for k, v in out["parts_us"].items()))
     print(json.dumps(out), flush=True)
 
 

@@ -49,6 +49,14 @@ def lib() -> ctypes.CDLL:
             "hbl_gemm_dequant": (I, [P, P, P, P, I64, I64, I64, I, P, P]),
             "hbl_forward": (I, [P, I, P, P, I64, I64, I64, I, I, I, P, F, P, P, SZ, P]),
             "hbl_swiglu": (I, [P, P, I64, P, P]),
+            "hbl_packed_weight_fp4_bytes": (SZ, [I64, I64]),
+            "hbl_packed_act_fp6_bytes": (SZ, [I64, I64]),
+            "hbl_forward_fp6fp4_workspace_bytes": (SZ, [I64, I64]),
+            "hbl_weights_to_fp4": (I, [P, I64, I64, P, P]),
+            "hbl_quantize_activations_fp6": (I, [P, I, I64, I64, I, P, F, I, P, P, P]),
+            "hbl_gemm_fp6fp4_s32": (I, [P, P, I64, I64, I64, P, P]),
+            "hbl_gemm_fp6fp4_dequant": (I, [P, P, P, P, I64, I64, I64, P, P]),
+            "hbl_forward_fp6fp4": (I, [P, I, P, P, I64, I64, I64, I, I, P, F, P, P, SZ, P]),
             "hbl_status_string": (ctypes.c_char_p, [I]),
             "hbl_last_error": (ctypes.c_char_p, []),
             "hbl_version": (I, []),
@@ -178,3 +186,70 @@ def swiglu(g, u, h=None):
         h = torch.empty_like(g)
     _check(lib().hbl_swiglu(_ptr(g), _ptr(u), g.numel(), _ptr(h), _stream()))
     return h
+
+
+# ---- FP6 x FP4 a4 path -------------------------------------------------------------------
+
+def weights_to_fp4(Wq, K: int):
+    """2-bit Wq [N, K/4] -> FP4 Wq4 [N, K/2] (the weight scale is unchanged)."""
+    import torch
+
+    _dev(Wq)
+    N = Wq.shape[0]
+    Wq4 = torch.empty((N, K // 2), dtype=torch.uint8, device=Wq.device)
+    _check(lib().hbl_weights_to_fp4(_ptr(Wq), N, K, _ptr(Wq4), _stream()))
+    return Wq4
+
+
+def quantize_activations_fp6(x, use_hadamard: bool, norm: bool = False, gamma=None, eps: float = 1e-5):
+    """x [M, K] -> (codes6 uint8 [M, 3K/4], deq fp32 [M]); the INT4 codes stored as FP6."""
+    import torch
+
+    _dev(x, gamma)
+    M, K = x.shape
+    codes = torch.empty((M, K // 4 * 3), dtype=torch.uint8, device=x.device)
+    deq = torch.empty(M, dtype=torch.float32, device=x.device)
+    _check(lib().hbl_quantize_activations_fp6(_ptr(x), _xdtype(x), M, K, HBL_NORM_RMS if norm else HBL_NORM_NONE,
+                                              _ptr(gamma), float(eps), int(bool(use_hadamard)), _ptr(codes),
+                                              _ptr(deq), _stream()))
+    return codes, deq
+
+
+def gemm_fp6fp4_s32(codes6, Wq4, K: int):
+    import torch
+
+    _dev(codes6, Wq4)
+    M, N = codes6.shape[0], Wq4.shape[0]
+    acc = torch.empty((M, N), dtype=torch.int32, device=codes6.device)
+    _check(lib().hbl_gemm_fp6fp4_s32(_ptr(codes6), _ptr(Wq4), M, K, N, _ptr(acc), _stream()))
+    return acc
+
+
+def gemm_fp6fp4_dequant(codes6, deq, Wq4, w_scale, K: int, y=None):
+    import torch
+
+    _dev(codes6, deq, Wq4, w_scale, y)
+    M, N = codes6.shape[0], Wq4.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=codes6.device)
+    _check(lib().hbl_gemm_fp6fp4_dequant(_ptr(codes6), _ptr(deq), _ptr(Wq4), _ptr(w_scale), M, K, N, _ptr(y),
+                                         _stream()))
+    return y
+
+
+def forward_fp6fp4(x, Wq4, w_scale, use_hadamard: bool, norm: bool = False, gamma=None, eps: float = 1e-5,
+                   y=None, ws=None):
+    import torch
+
+    _dev(x, Wq4, w_scale, gamma, y, ws)
+    M, K = x.shape
+    N = Wq4.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    if ws is None:
+        n = lib().hbl_forward_fp6fp4_workspace_bytes(M, K)
+        ws = torch.empty(max(n, 256), dtype=torch.uint8, device=x.device)
+    _check(lib().hbl_forward_fp6fp4(_ptr(x), _xdtype(x), _ptr(Wq4), _ptr(w_scale), M, K, N,
+                                    int(bool(use_hadamard)), HBL_NORM_RMS if norm else HBL_NORM_NONE, _ptr(gamma),
+                                    float(eps), _ptr(y), _ptr(ws), ws.numel(), _stream()))
+    return y

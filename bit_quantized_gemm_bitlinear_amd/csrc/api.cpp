@@ -211,6 +211,122 @@ hbl_status hbl_forward(const void* x, hbl_dtype xt, const uint8_t* Wq, const flo
   }
 }
 
+size_t hbl_packed_weight_fp4_bytes(int64_t N, int64_t K) {
+  if (N < 1 || K < 64 || K % 64 != 0 || K > HBL_MAX_K || N > INT32_MAX) return 0;
+  return (size_t)(N * (K / 2));
+}
+
+size_t hbl_packed_act_fp6_bytes(int64_t M, int64_t K) {
+  if (M < 0 || K < 64 || K % 64 != 0 || K > HBL_MAX_K || M > INT32_MAX) return 0;
+  return (size_t)(M * (K / 4) * 3);
+}
+
+size_t hbl_forward_fp6fp4_workspace_bytes(int64_t M, int64_t K) {
+  if (M < 0 || K < 64 || K % 64 != 0 || K > HBL_MAX_K || M > INT32_MAX) return 0;
+  return round256((size_t)(M * (K / 4) * 3)) + round256((size_t)M * sizeof(float));
+}
+
+hbl_status hbl_weights_to_fp4(const uint8_t* Wq, int64_t N, int64_t K, uint8_t* Wq4, void* stream) {
+  static const char* fn = "hbl_weights_to_fp4";
+  try {
+    if (N < 1 || N > INT32_MAX) return fail(HBL_ERR_INVALID_ARG, fn, "N must be in [1, 2^31)");
+    HBL_TRY(check_shape(fn, 0, K, N, 4));
+    HBL_TRY(check_ptr(fn, Wq, "Wq", 16));
+    HBL_TRY(check_ptr(fn, Wq4, "Wq4", 16));
+    hipError_t e = hbl::launch_weights_fp4(Wq, N, K, Wq4, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return HBL_OK;
+  } catch (...) {
+    return fail(HBL_ERR_HIP, fn, "unexpected C++ exception");
+  }
+}
+
+hbl_status hbl_quantize_activations_fp6(const void* x, hbl_dtype xt, int64_t M, int64_t K, hbl_norm norm,
+                                        const float* gamma, float norm_eps, int use_hadamard, uint8_t* codes6,
+                                        float* deq, void* stream) {
+  static const char* fn = "hbl_quantize_activations_fp6";
+  try {
+    HBL_TRY(check_shape(fn, M, K, -1, 4));
+    HBL_TRY(check_act(fn, xt, norm, gamma, norm_eps, use_hadamard, K));
+    if (M == 0) return HBL_OK;
+    HBL_TRY(check_ptr(fn, x, "x", 16));
+    HBL_TRY(check_ptr(fn, codes6, "codes6", 16));
+    HBL_TRY(check_ptr(fn, deq, "deq", 4));
+    hipError_t e = hbl::launch_actquant(x, (int)xt, M, K, (int)norm, norm == HBL_NORM_RMS ? gamma : nullptr,
+                                        norm_eps, 6, use_hadamard, codes6, deq, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return HBL_OK;
+  } catch (...) {
+    return fail(HBL_ERR_HIP, fn, "unexpected C++ exception");
+  }
+}
+
+hbl_status hbl_gemm_fp6fp4_s32(const uint8_t* codes6, const uint8_t* Wq4, int64_t M, int64_t K, int64_t N,
+                               int32_t* acc, void* stream) {
+  static const char* fn = "hbl_gemm_fp6fp4_s32";
+  try {
+    HBL_TRY(check_shape(fn, M, K, N, 4));
+    HBL_TRY(check_ptr(fn, Wq4, "Wq4", 16));
+    if (M == 0) return HBL_OK;
+    HBL_TRY(check_ptr(fn, codes6, "codes6", 16));
+    HBL_TRY(check_ptr(fn, acc, "acc", 16));
+    hipError_t e = hbl::launch_gemm_f6f4(codes6, nullptr, Wq4, nullptr, M, K, N, acc, nullptr, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return HBL_OK;
+  } catch (...) {
+    return fail(HBL_ERR_HIP, fn, "unexpected C++ exception");
+  }
+}
+
+hbl_status hbl_gemm_fp6fp4_dequant(const uint8_t* codes6, const float* deq, const uint8_t* Wq4, const float* w_scale,
+                                   int64_t M, int64_t K, int64_t N, float* y, void* stream) {
+  static const char* fn = "hbl_gemm_fp6fp4_dequant";
+  try {
+    HBL_TRY(check_shape(fn, M, K, N, 4));
+    HBL_TRY(check_ptr(fn, Wq4, "Wq4", 16));
+    HBL_TRY(check_ptr(fn, w_scale, "w_scale", 4));
+    if (M == 0) return HBL_OK;
+    HBL_TRY(check_ptr(fn, codes6, "codes6", 16));
+    HBL_TRY(check_ptr(fn, deq, "deq", 4));
+    HBL_TRY(check_ptr(fn, y, "y", 16));
+    hipError_t e = hbl::launch_gemm_f6f4(codes6, deq, Wq4, w_scale, M, K, N, nullptr, y, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return HBL_OK;
+  } catch (...) {
+    return fail(HBL_ERR_HIP, fn, "unexpected C++ exception");
+  }
+}
+
+hbl_status hbl_forward_fp6fp4(const void* x, hbl_dtype xt, const uint8_t* Wq4, const float* w_scale, int64_t M,
+                              int64_t K, int64_t N, int use_hadamard, hbl_norm norm, const float* gamma,
+                              float norm_eps, float* y, void* ws, size_t ws_bytes, void* stream) {
+  static const char* fn = "hbl_forward_fp6fp4";
+  try {
+    HBL_TRY(check_shape(fn, M, K, N, 4));
+    HBL_TRY(check_act(fn, xt, norm, gamma, norm_eps, use_hadamard, K));
+    HBL_TRY(check_ptr(fn, Wq4, "Wq4", 16));
+    HBL_TRY(check_ptr(fn, w_scale, "w_scale", 4));
+    if (M == 0) return HBL_OK;
+    HBL_TRY(check_ptr(fn, x, "x", 16));
+    HBL_TRY(check_ptr(fn, y, "y", 16));
+    const size_t need = hbl_forward_fp6fp4_workspace_bytes(M, K);
+    if (ws == nullptr || ws_bytes < need)
+      return fail(HBL_ERR_WORKSPACE, fn, "workspace missing or smaller than hbl_forward_fp6fp4_workspace_bytes");
+    HBL_TRY(check_ptr(fn, ws, "ws", 256));
+    uint8_t* codes = static_cast<uint8_t*>(ws);
+    float* deq = reinterpret_cast<float*>(codes + round256((size_t)(M * (K / 4) * 3)));
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = hbl::launch_actquant(x, (int)xt, M, K, (int)norm, norm == HBL_NORM_RMS ? gamma : nullptr,
+                                        norm_eps, 6, use_hadamard, codes, deq, s);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    e = hbl::launch_gemm_f6f4(codes, deq, Wq4, w_scale, M, K, N, nullptr, y, s);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return HBL_OK;
+  } catch (...) {
+    return fail(HBL_ERR_HIP, fn, "unexpected C++ exception");
+  }
+}
+
 hbl_status hbl_swiglu(const float* g, const float* u, int64_t n, float* h, void* stream) {
   static const char* fn = "hbl_swiglu";
   try {

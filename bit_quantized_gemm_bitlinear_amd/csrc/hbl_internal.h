@@ -11,7 +11,8 @@ namespace hbl {
 hipError_t launch_wquant(const float* W, int64_t N, int64_t K, uint8_t* Wq, float* w_scale, double* ws,
                          hipStream_t s);
 
-// Activation quantisation (k_actquant.hip).  xt: 0 fp32, 1 bf16.
+// Activation quantisation (k_actquant.hip).  xt: 0 fp32, 1 bf16.  abits: 4 (INT4 nibbles),
+// 8 (INT8) or 6 (INT4 values stored as FP6 E2M3 codes).
 hipError_t launch_actquant(const void* x, int xt, int64_t M, int64_t K, int norm, const float* gamma,
                            float eps, int abits, int use_h, uint8_t* codes, float* deq, hipStream_t s);
 
@@ -19,6 +20,12 @@ hipError_t launch_actquant(const void* x, int xt, int64_t M, int64_t K, int norm
 // (y != nullptr) (k_gemm.hip).
 hipError_t launch_gemm(const uint8_t* codes, const float* deq, const uint8_t* Wq, const float* w_scale,
                        int64_t M, int64_t K, int64_t N, int abits, int32_t* acc, float* y, hipStream_t s);
+
+// GEMM of FP6-coded INT4 activations with FP4-coded ternary weights (k_gemm_f6f4.hip).
+hipError_t launch_gemm_f6f4(const uint8_t* codes6, const float* deq, const uint8_t* Wq4, const float* w_scale,
+                            int64_t M, int64_t K, int64_t N, int32_t* acc, float* y, hipStream_t s);
+// 2-bit ternary words -> FP4 E2M1 nibbles (k_gemm_f6f4.hip).
+hipError_t launch_weights_fp4(const uint8_t* Wq, int64_t N, int64_t K, uint8_t* Wq4, hipStream_t s);
 
 // h = silu(g) * u (k_swiglu.hip).
 hipError_t launch_swiglu(const float* g, const float* u, int64_t n, float* h, hipStream_t s);

@@ -117,10 +117,33 @@ __device__ __forceinline__ double row_sum(double v, double* red) {
   }
 }
 
+// ABITS: 4 = INT4 codes packed as nibbles, 8 = INT8 codes, 6 = INT4 codes (Qb = 7) stored as
+// FP6 E2M3 (6 bits each, code k at bits [6k, 6k+6) of the row's little-endian bit string).
 template <int ABITS>
 struct QB {
-  static constexpr float value = ABITS == 4 ? 7.0f : 127.0f;
+  static constexpr float value = ABITS == 8 ? 127.0f : 7.0f;
 };
+
+template <int ABITS>
+constexpr int row_bytes(int K) { return ABITS == 4 ? K / 2 : (ABITS == 8 ? K : K * 6 / 8); }
+
+typedef float v16f_t __attribute__((ext_vector_type(16)));
+
+// 2 to 32 integer-valued floats (|q| <= 7) -> FP6 E2M3, packed 6 bits each in element order.
+// The hardware conversion interleaves its two 16-wide operands (element 2i from the first,
+// 2i+1 from the second); the scale 1.0 leaves values unscaled.  Exact for these integers.
+template <int NV>
+__device__ __forceinline__ void fp6_pack(const float* q, uint32_t (&w)[6]) {
+  v16f_t ev, od;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    ev[i] = 2 * i < NV ? q[2 * i] : 0.0f;
+    od[i] = 2 * i + 1 < NV ? q[2 * i + 1] : 0.0f;
+  }
+  const auto r = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, 1.0f);
+#pragma unroll
+  for (int i = 0; i < 6; ++i) w[i] = (uint32_t)r[i];
+}
 
 // Store NWORDS packed 32-bit words to dst (aligned to 4 * min(NWORDS, 4) bytes).
 template <int NWORDS>
@@ -150,7 +173,31 @@ __device__ __forceinline__ uint32_t rne_bits(float v, float magic) { return __fl
 template <int ABITS, int RL>
 __device__ __forceinline__ void store_run(const float* v, float s, uint8_t* __restrict__ crow, int k0) {
   constexpr float MAGIC = 12582912.0f;  // 1.5 * 2^23
-  if constexpr (ABITS == 4) {
+  if constexpr (ABITS == 6) {
+    // rint first (the FP6 grid is finer than the integers below 4), then the exact conversion.
+    uint8_t* dst = crow + (k0 / 8) * 6;
+#pragma unroll
+    for (int c = 0; c < RL; c += 32) {
+      constexpr int NV = RL < 32 ? RL : 32;
+      float q[NV];
+#pragma unroll
+      for (int i = 0; i < NV; ++i) q[i] = __builtin_rintf(v[c + i] * s) + 0.0f;  // +0.0f: -0 -> +0 (code 0x00)
+      uint32_t w[6];
+      fp6_pack<NV>(q, w);
+      if constexpr (NV == 32) {
+#pragma unroll
+        for (int i = 0; i < 3; ++i) reinterpret_cast<uint2*>(dst + 24 * (c / 32))[i] = make_uint2(w[2 * i], w[2 * i + 1]);
+      } else if constexpr (NV == 16) {
+#pragma unroll
+        for (int i = 0; i < 3; ++i) reinterpret_cast<uint32_t*>(dst)[i] = w[i];
+      } else {  // 8 codes = 48 bits, 2-byte aligned
+        uint16_t* d16 = reinterpret_cast<uint16_t*>(dst);
+        d16[0] = (uint16_t)(w[0] & 0xffffu);
+        d16[1] = (uint16_t)(w[0] >> 16);
+        d16[2] = (uint16_t)(w[1] & 0xffffu);
+      }
+    }
+  } else if constexpr (ABITS == 4) {
     uint32_t w[RL / 8];
 #pragma unroll
     for (int d = 0; d < RL / 8; ++d) {
@@ -322,7 +369,7 @@ __global__ __launch_bounds__(block_threads<L>()) void k_actquant_h(
     const bool zero = amax < 0x1p-120f;     // also keeps Qb / amax finite
     const float s = zero ? 0.0f : Qb / amax;  // s = 0 quantises the whole row to 0
     if (valid) {
-      uint8_t* crow = codes + row * (int64_t)(K * ABITS / 8);
+      uint8_t* crow = codes + row * (int64_t)row_bytes<ABITS>(K);
       constexpr int LASTP = NP - 1;
       using LY = Layout<L, LASTP>;
       constexpr int RL = NP == 1 ? 64 : (1 << LY::c);  // run of consecutive elements in registers
@@ -409,9 +456,11 @@ __global__ __launch_bounds__(256) void k_actquant_plain(const void* __restrict__
   constexpr float Qb = QB<ABITS>::value;
   const bool zero = amax < 0x1p-120f;
   const float s = zero ? 0.0f : Qb / amax;
-  uint8_t* crow = codes + row * (K * ABITS / 8);
+  uint8_t* crow = codes + row * (int64_t)row_bytes<ABITS>((int)K);
   auto put = [&](int ch, const float* o) {
-    if constexpr (ABITS == 4) {
+    if constexpr (ABITS == 6) {
+      store_run<6, 8>(o, s, crow, 8 * ch);
+    } else if constexpr (ABITS == 4) {
       *reinterpret_cast<uint32_t*>(crow + 4 * ch) =
           pack8_a4(rne_int(o[0] * s), rne_int(o[1] * s), rne_int(o[2] * s), rne_int(o[3] * s),
                    rne_int(o[4] * s), rne_int(o[5] * s), rne_int(o[6] * s), rne_int(o[7] * s));
@@ -506,12 +555,18 @@ hipError_t launch_actquant(const void* x, int xt, int64_t M, int64_t K, int norm
     if (abits == 4)
       return xt ? dispatch_h<4, 1>(L, x, M, gamma, eps, norm, codes, deq, s)
                 : dispatch_h<4, 0>(L, x, M, gamma, eps, norm, codes, deq, s);
+    if (abits == 6)
+      return xt ? dispatch_h<6, 1>(L, x, M, gamma, eps, norm, codes, deq, s)
+                : dispatch_h<6, 0>(L, x, M, gamma, eps, norm, codes, deq, s);
     return xt ? dispatch_h<8, 1>(L, x, M, gamma, eps, norm, codes, deq, s)
               : dispatch_h<8, 0>(L, x, M, gamma, eps, norm, codes, deq, s);
   }
   if (abits == 4)
     return xt ? dispatch_plain<4, 1>(x, M, K, gamma, eps, norm, codes, deq, s)
               : dispatch_plain<4, 0>(x, M, K, gamma, eps, norm, codes, deq, s);
+  if (abits == 6)
+    return xt ? dispatch_plain<6, 1>(x, M, K, gamma, eps, norm, codes, deq, s)
+              : dispatch_plain<6, 0>(x, M, K, gamma, eps, norm, codes, deq, s);
   return xt ? dispatch_plain<8, 1>(x, M, K, gamma, eps, norm, codes, deq, s)
             : dispatch_plain<8, 0>(x, M, K, gamma, eps, norm, codes, deq, s);
 }

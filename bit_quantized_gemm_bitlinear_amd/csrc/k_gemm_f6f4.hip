@@ -1,0 +1,257 @@
+// k_gemm_f6f4.hip — the a4 GEMM on gfx950's scaled f8f6f4 matrix cores: INT4 activation
+// codes stored as FP6 (E2M3) times ternary weights stored as FP4 (E2M1).
+//
+// The pages motivate 4-bit activations by hardware that computes natively in 4 bits
+// (BitNet v2 write-up, section "原生4比特計算").  On MI355X the FP6/FP4 matrix path runs at
+// twice the int8 rate.  Every INT4 code in [-7, 7] is exact in FP6 E2M3 and every ternary
+// weight is exact in FP4 E2M1, each product is an integer of magnitude <= 7, and the fp32
+// accumulator holds integer partial sums below 2^24 for K <= 2^21, so every sum is exact
+// regardless of order: the result equals the int32 product bit for bit.  Block scales are
+// fixed at 1 (E8M0 exponent 127).  No operand is decoded in this kernel; LDS fragments go
+// straight into v_mfma_scale_f32_32x32x64_f8f6f4 (lane l: row / column l%32, the 32 k-values
+// 32*(l/32) .. +31 of the 64-deep step; A as 6 registers of packed 6-bit codes, B as 4
+// registers of packed nibbles).
+//
+// Tiling follows the int8 kernel: 256 x 256 block tile, 8 waves of 128 x 64, K staged through
+// double-buffered LDS 128 deep, fragments read one k-step ahead.
+#include "hbl_device.h"
+#include "hbl_internal.h"
+
+namespace hbl {
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+constexpr int BK6 = 128;
+
+__device__ __forceinline__ void tile_order(int bid, int nblk, int ntm, int ntn, int GM, int& tm, int& tn) {
+  constexpr int NXCD = 8;
+  int t = bid;
+  const int per = nblk / NXCD;
+  if (bid < per * NXCD) t = (bid % NXCD) * per + bid / NXCD;
+  const int group = t / (GM * ntn);
+  const int first = group * GM;
+  const int gm = min(ntm - first, GM);
+  const int r = t - group * GM * ntn;
+  tm = first + r % gm;
+  tn = r / gm;
+}
+
+template <int BM, int BN, int WR, int WC, int MODE>
+__global__ __launch_bounds__(64 * WR * WC) void k_gemm_f6f4(const uint8_t* __restrict__ A,
+                                                            const float* __restrict__ deq,
+                                                            const uint8_t* __restrict__ B,
+                                                            const float* __restrict__ w_scale, int M, int N, int K,
+                                                            int32_t* __restrict__ acc_out, float* __restrict__ y) {
+  constexpr int NT = 64 * WR * WC;
+  constexpr int KS = BK6 / 64;                // 64-deep MFMA steps per stage
+  constexpr int AB = BK6 * 6 / 8;             // 96 bytes of FP6 codes per row per stage
+  constexpr int AS = AB + 8;                  // 104: 26 dwords, distinct even banks for 16 rows
+  constexpr int BB = BK6 / 2;                 // 64 bytes of FP4 weights per row per stage
+  constexpr int BS = BB + 16;                 // 80: 20 dwords, distinct 4-bank groups for 8 rows
+  constexpr int WM = BM / WR, WN = BN / WC;
+  constexpr int TM = WM / 32, TN = WN / 32;
+  constexpr int ACH = AB / 16, BCH = BB / 16;
+  constexpr int ALD = BM * ACH / NT, BLD = BN * BCH / NT;
+  static_assert(ALD * NT == BM * ACH && BLD * NT == BN * BCH, "tile/thread mismatch");
+  static_assert(KS % 2 == 0, "even k-steps per stage");
+
+  __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * AS];
+  __shared__ __attribute__((aligned(16))) uint8_t sB[2][BN * BS];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WC, wn = wave % WC;
+  const int ntm = (M + BM - 1) / BM, ntn = (N + BN - 1) / BN;
+  int tm, tn;
+  tile_order(blockIdx.x, gridDim.x, ntm, ntn, 4, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int64_t arow = (int64_t)K * 6 / 8;
+  const int64_t brow = K / 2;
+  const int KT = (K + BK6 - 1) / BK6;
+  const int last_k64 = (K - (KT - 1) * BK6) / 64;
+
+  const uint8_t* Ablk = A + (int64_t)m0 * arow;
+  const uint8_t* Bblk = B + (int64_t)n0 * brow;
+  uint32_t aoff[ALD], boff[BLD];
+#pragma unroll
+  for (int i = 0; i < ALD; ++i) {
+    const int e = tid + NT * i, r = e / ACH, c = e % ACH;
+    aoff[i] = (uint32_t)(min(r, M - 1 - m0) * arow + 16 * c);
+  }
+#pragma unroll
+  for (int i = 0; i < BLD; ++i) {
+    const int e = tid + NT * i, r = e / BCH, c = e % BCH;
+    boff[i] = (uint32_t)(min(r, N - 1 - n0) * brow + 16 * c);
+  }
+
+  uint4 ra[ALD], rb[BLD];
+  // Stage kt; in a partial last stage only the first n64 64-deep slices exist and the rest
+  // is zero-filled (a zero FP4 weight contributes nothing).
+  auto gload = [&](int kt, int n64) {
+    const int va = n64 * 48 / 16, vb = n64 * 32 / 16;
+    const uint8_t* ak = Ablk + (int64_t)kt * AB;
+    const uint8_t* bk = Bblk + (int64_t)kt * BB;
+#pragma unroll
+    for (int i = 0; i < ALD; ++i)
+      ra[i] = (int)((tid + NT * i) % ACH) < va ? *reinterpret_cast<const uint4*>(ak + aoff[i]) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < BLD; ++i)
+      rb[i] = (int)((tid + NT * i) % BCH) < vb ? *reinterpret_cast<const uint4*>(bk + boff[i]) : make_uint4(0, 0, 0, 0);
+  };
+  auto swrite = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < ALD; ++i) {
+      const int e = tid + NT * i;
+      uint8_t* d = &sA[buf][(e / ACH) * AS + 16 * (e % ACH)];
+      reinterpret_cast<uint2*>(d)[0] = make_uint2(ra[i].x, ra[i].y);
+      reinterpret_cast<uint2*>(d)[1] = make_uint2(ra[i].z, ra[i].w);
+    }
+#pragma unroll
+    for (int i = 0; i < BLD; ++i) {
+      const int e = tid + NT * i;
+      *reinterpret_cast<uint4*>(&sB[buf][(e / BCH) * BS + 16 * (e % BCH)]) = rb[i];
+    }
+  };
+
+  struct Frag {
+    uint2 a[TM][3];   // 24 bytes: 32 FP6 codes
+    uint4 b[TN];      // 16 bytes: 32 FP4 weights
+  };
+  const int arow0 = (wm * WM + (lane & 31)) * AS + 24 * (lane >> 5);
+  const int brow0 = (wn * WN + (lane & 31)) * BS + 16 * (lane >> 5);
+  auto fread = [&](int buf, int ks, Frag& f) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const uint2* p = reinterpret_cast<const uint2*>(&sA[buf][arow0 + 32 * i * AS + ks * 48]);
+      f.a[i][0] = p[0];
+      f.a[i][1] = p[1];
+      f.a[i][2] = p[2];
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) f.b[j] = *reinterpret_cast<const uint4*>(&sB[buf][brow0 + 32 * j * BS + ks * 32]);
+  };
+
+  v16f acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = v16f{};
+
+  auto fmma = [&](const Frag& f) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const v8i a = v8i{(int)f.a[i][0].x, (int)f.a[i][0].y, (int)f.a[i][1].x, (int)f.a[i][1].y,
+                        (int)f.a[i][2].x, (int)f.a[i][2].y, 0, 0};
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const v8i b = v8i{(int)f.b[j].x, (int)f.b[j].y, (int)f.b[j].z, (int)f.b[j].w, 0, 0, 0, 0};
+        // cbsz = 2: A is FP6 E2M3; blgp = 4: B is FP4 E2M1; scales 127 = 2^0.
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[i][j], 2, 4, 0, 127, 0, 127);
+      }
+    }
+  };
+
+  Frag f0, f1;
+  gload(0, KT == 1 ? last_k64 : KS);
+  swrite(0);
+  __syncthreads();
+  fread(0, 0, f0);
+  for (int kt = 0; kt < KT; ++kt) {
+    const int buf = kt & 1;
+    const bool has_next = kt + 1 < KT;
+    if (has_next) gload(kt + 1, kt + 1 == KT - 1 ? last_k64 : KS);
+#pragma unroll
+    for (int ks = 0; ks < KS; ks += 2) {
+      fread(buf, ks + 1, f1);
+      fmma(f0);
+      if (ks + 2 < KS) fread(buf, ks + 2, f0);
+      fmma(f1);
+    }
+    if (has_next) swrite(buf ^ 1);
+    __syncthreads();
+    if (has_next) fread(buf ^ 1, 0, f0);
+  }
+
+  float alpha = 0.0f;
+  if constexpr (MODE == 1) alpha = w_scale[0];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int m = m0 + wm * WM + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      if (m >= M) continue;
+      float dm = 0.0f;
+      if constexpr (MODE == 1) dm = deq[m];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int n = n0 + wn * WN + 32 * j + (lane & 31);
+        if (n >= N) continue;
+        const float a = acc[i][j][v];  // an exact integer
+        if constexpr (MODE == 0) {
+          acc_out[(int64_t)m * N + n] = (int32_t)a;
+        } else {
+          y[(int64_t)m * N + n] = __fmul_rn(__fmul_rn(a, dm), alpha);
+        }
+      }
+    }
+  }
+}
+
+template <int BM, int BN, int WR, int WC, int MODE>
+hipError_t launch_cfg(const uint8_t* codes, const float* deq, const uint8_t* Wq4, const float* w_scale, int64_t M,
+                      int64_t K, int64_t N, int32_t* acc, float* y, hipStream_t s) {
+  const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  hipLaunchKernelGGL((k_gemm_f6f4<BM, BN, WR, WC, MODE>), dim3((unsigned)tiles), dim3(64 * WR * WC), 0, s, codes,
+                     deq, Wq4, w_scale, (int)M, (int)N, (int)K, acc, y);
+  return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t launch(const uint8_t* codes, const float* deq, const uint8_t* Wq4, const float* w_scale, int64_t M,
+                  int64_t K, int64_t N, int32_t* acc, float* y, hipStream_t s) {
+  constexpr int64_t CUS = 256;
+  const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
+  const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
+  if ((double)((t256 + CUS - 1) / CUS) * 2.0 <= (double)((t128 + CUS - 1) / CUS))
+    return launch_cfg<256, 256, 2, 4, MODE>(codes, deq, Wq4, w_scale, M, K, N, acc, y, s);
+  return launch_cfg<128, 128, 2, 2, MODE>(codes, deq, Wq4, w_scale, M, K, N, acc, y, s);
+}
+
+// Ternary 2-bit words (16 weights, weight c in field 4(c%4)+c/4) -> FP4 E2M1 nibbles in
+// natural order (weight c in nibble c): 0 -> 0x0, +1 -> 0x2 (1.0), -1 -> 0xA (-1.0).
+__global__ __launch_bounds__(256) void k_weights_fp4(const uint32_t* __restrict__ Wq, int64_t words,
+                                                     uint2* __restrict__ Wq4) {
+  for (int64_t w = (int64_t)blockIdx.x * 256 + threadIdx.x; w < words; w += (int64_t)gridDim.x * 256) {
+    const uint32_t src = Wq[w];
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      const uint32_t f = (src >> (2 * (4 * (c & 3) + (c >> 2)))) & 3u;  // 00 = 0, 01 = +1, 11 = -1
+      const uint32_t nib = f == 1u ? 0x2u : (f == 3u ? 0xAu : 0x0u);
+      if (c < 8) lo |= nib << (4 * c);
+      else hi |= nib << (4 * (c - 8));
+    }
+    Wq4[w] = make_uint2(lo, hi);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_f6f4(const uint8_t* codes6, const float* deq, const uint8_t* Wq4, const float* w_scale,
+                            int64_t M, int64_t K, int64_t N, int32_t* acc, float* y, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  if (acc != nullptr) return launch<0>(codes6, deq, Wq4, w_scale, M, K, N, acc, y, s);
+  return launch<1>(codes6, deq, Wq4, w_scale, M, K, N, acc, y, s);
+}
+
+hipError_t launch_weights_fp4(const uint8_t* Wq, int64_t N, int64_t K, uint8_t* Wq4, hipStream_t s) {
+  const int64_t words = N * K / 16;
+  int64_t blocks = (words + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(k_weights_fp4, dim3((unsigned)blocks), dim3(256), 0, s, reinterpret_cast<const uint32_t*>(Wq),
+                     words, reinterpret_cast<uint2*>(Wq4));
+  return hipGetLastError();
+}
+
+}  // namespace hbl

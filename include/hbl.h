@@ -62,6 +62,17 @@
  *
  *  deq — one fp32 per row.
  *
+ *  FP6/FP4 variant of the a4 path (gfx950's scaled f8f6f4 matrix cores run FP6 x FP4 at
+ *  twice the int8 rate; every INT4 code in [-7, 7] and every ternary weight is exact in
+ *  these formats, so results are identical to the INT4/2-bit path):
+ *  codes6 — the same INT4 absmax codes (Qb = 7), M rows of 3K/4 bytes; code k of a row sits
+ *       at bits [6k, 6k+6) of the row read as a little-endian bit string, encoded as OCP FP6
+ *       E2M3 (bit 5 sign, bits 4..3 exponent with bias 1, bits 2..0 mantissa): 0 -> 0x00,
+ *       1 -> 0x08, 2 -> 0x10, 3 -> 0x14, 4 -> 0x18, 5 -> 0x1A, 6 -> 0x1C, 7 -> 0x1E, and
+ *       -q -> 0x20 | code(q).
+ *  Wq4  — ternary weights as OCP FP4 E2M1, N rows of K/2 bytes; weight k of a row in nibble
+ *       k (low nibble first): 0 -> 0x0, +1 -> 0x2, -1 -> 0xA.
+ *
  * Conventions for every entry point:
  *  - Every pointer argument is a device pointer (hipMalloc / torch CUDA memory) unless
  *    stated otherwise, 16-byte aligned.  The caller owns every buffer; the library never
@@ -158,6 +169,35 @@ hbl_status hbl_forward(const void* x, hbl_dtype xt, const uint8_t* Wq, const flo
  *  h[i] = fl32( silu(g[i]) * u[i] ),  silu(v) = v / (1 + exp(-v)) in fp32.
  *  g, u, h: n fp32 each; h may alias neither g nor u.  n >= 0. */
 hbl_status hbl_swiglu(const float* g, const float* u, int64_t n, float* h, void* stream);
+
+/* ---- FP6 x FP4 a4 path ----------------------------------------------------------------
+ * The same layer with the a4 codes stored as FP6 and the weights as FP4 (formats above);
+ * outputs are bit-identical to the INT4 / 2-bit calls.  Written for the 4-bit matrix
+ * hardware the BitNet v2 write-up motivates a4 with (section "原生4比特計算"). */
+size_t hbl_packed_weight_fp4_bytes(int64_t N, int64_t K);         /* N*K/2          */
+size_t hbl_packed_act_fp6_bytes(int64_t M, int64_t K);            /* M*K*3/4        */
+size_t hbl_forward_fp6fp4_workspace_bytes(int64_t M, int64_t K);
+
+/* Wq (2-bit, from hbl_quantize_weights) -> Wq4 [N, K/2] FP4.  w_scale is unchanged. */
+hbl_status hbl_weights_to_fp4(const uint8_t* Wq, int64_t N, int64_t K, uint8_t* Wq4, void* stream);
+
+/* As hbl_quantize_activations with abits = 4, writing codes6 [M, 3K/4] instead of nibbles. */
+hbl_status hbl_quantize_activations_fp6(const void* x, hbl_dtype xt, int64_t M, int64_t K, hbl_norm norm,
+                                        const float* gamma, float norm_eps, int use_hadamard, uint8_t* codes6,
+                                        float* deq, void* stream);
+
+/* Integer product of codes6 and Wq4 (exact; acc [M, N] int32), and with the dequant epilogue
+ * (y [M, N] fp32, same association as hbl_gemm_dequant). */
+hbl_status hbl_gemm_fp6fp4_s32(const uint8_t* codes6, const uint8_t* Wq4, int64_t M, int64_t K, int64_t N,
+                               int32_t* acc, void* stream);
+hbl_status hbl_gemm_fp6fp4_dequant(const uint8_t* codes6, const float* deq, const uint8_t* Wq4,
+                                   const float* w_scale, int64_t M, int64_t K, int64_t N, float* y,
+                                   void* stream);
+
+/* The whole a4 forward on the FP6 x FP4 path; ws >= hbl_forward_fp6fp4_workspace_bytes(M, K). */
+hbl_status hbl_forward_fp6fp4(const void* x, hbl_dtype xt, const uint8_t* Wq4, const float* w_scale, int64_t M,
+                              int64_t K, int64_t N, int use_hadamard, hbl_norm norm, const float* gamma,
+                              float norm_eps, float* y, void* ws, size_t ws_bytes, void* stream);
 
 /* Static text for a status code, and the detail of the last failure on this thread. */
 const char* hbl_status_string(hbl_status s);

@@ -20,6 +20,9 @@ from .oracle import (  # noqa: F401
     lib_path,
     num_threads,
     pack_codes,
+    pack_codes_fp6,
+    pack_weights_fp4,
+    unpack_codes_fp6,
     pack_weights,
     quantize_activations,
     quantize_weights,

@@ -352,3 +352,79 @@ int orc_unpack_codes(const uint8_t* codes, int64_t M, int64_t K, int abits, int8
       }
   return 0;
 }
+
+/* ------------------------------------------------------------------------------------
+ * FP6 / FP4 storage of the same codes (the C ABI header documents the layouts).  The
+ * encodings follow the OCP microscaling element formats: FP6 E2M3 is sign | 2-bit
+ * exponent (bias 1) | 3-bit mantissa, value (-1)^s * 2^(e-1) * (1 + m/8) for e > 0 and
+ * (-1)^s * m/8 for e = 0; FP4 E2M1 is sign | 2-bit exponent (bias 1) | 1-bit mantissa.
+ * Only integers are encoded here (INT4 codes |q| <= 7, ternary weights), all exactly.
+ * ------------------------------------------------------------------------------------ */
+static unsigned fp6_e2m3_of_int(int q) {
+  unsigned sign = q < 0 ? 1u : 0u;
+  unsigned a = (unsigned)(q < 0 ? -q : q);
+  unsigned code;
+  if (a == 0) {
+    code = 0;
+  } else {
+    unsigned e = 0; /* floor(log2 a) */
+    while ((a >> (e + 1)) != 0) ++e;
+    /* a = 2^e * (1 + m/8)  =>  m = (a - 2^e) * 8 / 2^e, exact for a <= 7 */
+    unsigned m = ((a - (1u << e)) * 8u) >> e;
+    code = ((e + 1u) << 3) | m;
+  }
+  return (sign << 5) | code;
+}
+
+static int int_of_fp6_e2m3(unsigned code) {
+  unsigned e = (code >> 3) & 3u, m = code & 7u;
+  double v = e == 0 ? m / 8.0 : ldexp(1.0 + m / 8.0, (int)e - 1);
+  if (code & 0x20u) v = -v;
+  return (int)v;
+}
+
+int orc_pack_codes_fp6(const int8_t* q, int64_t M, int64_t K, uint8_t* out) {
+  if (M < 0 || K <= 0 || (K % 4) != 0) return -1;
+  const int64_t rb = K / 4 * 3;
+  for (int64_t m = 0; m < M; ++m) {
+    uint8_t* row = out + m * rb;
+    for (int64_t b = 0; b < rb; ++b) row[b] = 0;
+    for (int64_t k = 0; k < K; ++k) {
+      int qv = q[m * K + k];
+      if (qv < -7 || qv > 7) return -1;
+      unsigned c = fp6_e2m3_of_int(qv);
+      int64_t bit = 6 * k;
+      for (int i = 0; i < 6; ++i)
+        if ((c >> i) & 1u) row[(bit + i) / 8] |= (uint8_t)(1u << ((bit + i) % 8));
+    }
+  }
+  return 0;
+}
+
+int orc_unpack_codes_fp6(const uint8_t* codes, int64_t M, int64_t K, int8_t* q) {
+  if (M < 0 || K <= 0 || (K % 4) != 0) return -1;
+  const int64_t rb = K / 4 * 3;
+  for (int64_t m = 0; m < M; ++m)
+    for (int64_t k = 0; k < K; ++k) {
+      unsigned c = 0;
+      int64_t bit = 6 * k;
+      for (int i = 0; i < 6; ++i) c |= (unsigned)((codes[m * rb + (bit + i) / 8] >> ((bit + i) % 8)) & 1u) << i;
+      q[m * K + k] = (int8_t)int_of_fp6_e2m3(c);
+    }
+  return 0;
+}
+
+int orc_pack_weights_fp4(const int8_t* T, int64_t N, int64_t K, uint8_t* out) {
+  if (N <= 0 || K <= 0 || (K % 2) != 0) return -1;
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t k = 0; k < K; k += 2) {
+      unsigned nib[2];
+      for (int i = 0; i < 2; ++i) {
+        int t = T[n * K + k + i];
+        /* E2M1: 1.0 = exponent 1 (bias 1), mantissa 0 -> 0b0010; sign is bit 3 */
+        nib[i] = t == 0 ? 0u : ((t < 0 ? 8u : 0u) | 2u);
+      }
+      out[n * (K / 2) + k / 2] = (uint8_t)(nib[0] | (nib[1] << 4));
+    }
+  return 0;
+}

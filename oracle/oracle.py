@@ -75,6 +75,12 @@ def _load():
         lib.orc_pack_codes.restype = I
         lib.orc_unpack_codes.argtypes = [P, I64, I64, I, P]
         lib.orc_unpack_codes.restype = I
+        lib.orc_pack_codes_fp6.argtypes = [P, I64, I64, P]
+        lib.orc_pack_codes_fp6.restype = I
+        lib.orc_unpack_codes_fp6.argtypes = [P, I64, I64, P]
+        lib.orc_unpack_codes_fp6.restype = I
+        lib.orc_pack_weights_fp4.argtypes = [P, I64, I64, P]
+        lib.orc_pack_weights_fp4.restype = I
         _lib = lib
         return lib
 
@@ -231,6 +237,35 @@ def unpack_codes(codes, K: int, abits: int) -> np.ndarray:
     if _load().orc_unpack_codes(_p(codes), M, K, int(abits), _p(q)) != 0:
         raise ValueError("orc_unpack_codes: bad arguments")
     return q
+
+
+def pack_codes_fp6(q) -> np.ndarray:
+    """INT4 codes (|q| <= 7) -> FP6 E2M3, 6 bits per code, rows of 3K/4 bytes."""
+    q = _c(q, np.int8)
+    M, K = q.shape
+    out = np.empty((M, K // 4 * 3), np.uint8)
+    if _load().orc_pack_codes_fp6(_p(q), M, K, _p(out)) != 0:
+        raise ValueError("orc_pack_codes_fp6: bad arguments or code out of range")
+    return out
+
+
+def unpack_codes_fp6(codes, K: int) -> np.ndarray:
+    codes = _c(codes, np.uint8)
+    M = codes.shape[0]
+    q = np.empty((M, K), np.int8)
+    if _load().orc_unpack_codes_fp6(_p(codes), M, K, _p(q)) != 0:
+        raise ValueError("orc_unpack_codes_fp6: bad arguments")
+    return q
+
+
+def pack_weights_fp4(T) -> np.ndarray:
+    """Ternary weights -> FP4 E2M1 nibbles, weight k in nibble k (low first)."""
+    T = _c(T, np.int8)
+    N, K = T.shape
+    out = np.empty((N, K // 2), np.uint8)
+    if _load().orc_pack_weights_fp4(_p(T), N, K, _p(out)) != 0:
+        raise ValueError("orc_pack_weights_fp4: bad arguments")
+    return out
 
 
 def dense_reference(x, T, alpha: float, use_h: bool, norm: bool = False, gamma=None, eps: float = 1e-5):

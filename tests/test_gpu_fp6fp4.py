@@ -1,0 +1,103 @@
+"""Parity of the FP6 x FP4 a4 path (gfx950 scaled f8f6f4 matrix cores) against the oracle.
+
+The path stores the same INT4 absmax codes as FP6 E2M3 and the ternary weights as FP4 E2M1;
+every value is exact and the fp32 accumulation of integer products stays below 2^24, so the
+codes, the int32 product and the outputs must equal the INT4 / 2-bit path bit for bit."""
+import numpy as np
+import pytest
+
+from bit_quantized_gemm_bitlinear_amd import binding as B
+from bit_quantized_gemm_bitlinear_amd import inputs
+from tests.gpu_util import assert_close_ulps, note, rel_fro, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("N,K", [(3, 64), (257, 1024), (64, 16384)])
+def test_weights_to_fp4(orc, N, K):
+    note("weights fp4", N, K)
+    W = inputs.make_weights(N, K, seed=N)
+    T, _ = orc.quantize_weights(W)
+    Wq, _ = B.quantize_weights(to_dev(W))
+    np.testing.assert_array_equal(to_host(B.weights_to_fp4(Wq, K)), orc.pack_weights_fp4(T))
+
+
+@pytest.mark.parametrize("L", [6, 8, 9, 11, 12, 13, 14, 15])
+def test_actquant_fp6_codes(orc, L):
+    K = 1 << L
+    M = max(1, 256 // max(K // 64, 1)) + 3 if K <= 16384 else 5
+    M = min(M, 300)
+    note("actquant fp6", K, M)
+    x = inputs.make_activations("mixture", M, K, seed=L, outlier_frac=0.01, outlier_scale=50.0)
+    q, deq, _ = orc.quantize_activations(x, 4, True, norm=True)
+    codes, deq_d = B.quantize_activations_fp6(to_dev(x), True, norm=True)
+    np.testing.assert_array_equal(to_host(codes), orc.pack_codes_fp6(q))
+    assert_close_ulps(to_host(deq_d), deq, 2, "deq")
+
+
+@pytest.mark.parametrize("K", [64, 4096, 4160])
+def test_actquant_fp6_plain(orc, K):
+    note("actquant fp6 plain", K)
+    x = inputs.make_activations("normal", 9, K, seed=K, outlier_frac=0.01, outlier_scale=30.0)
+    q, deq, _ = orc.quantize_activations(x, 4, False, norm=False)
+    codes, deq_d = B.quantize_activations_fp6(to_dev(x), False, norm=False)
+    np.testing.assert_array_equal(to_host(codes), orc.pack_codes_fp6(q))
+    np.testing.assert_array_equal(to_host(deq_d), deq)
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 64, 1), (200, 320, 136), (129, 1024, 257), (64, 16384, 64),
+                                   (2500, 576, 2200)])
+def test_gemm_fp6fp4_s32(orc, M, K, N):
+    note("gemm fp6fp4", M, K, N)
+    rng = np.random.default_rng(M + N)
+    q = rng.integers(-7, 8, size=(M, K)).astype(np.int8)
+    T = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+    acc = to_host(B.gemm_fp6fp4_s32(to_dev(orc.pack_codes_fp6(q)), to_dev(orc.pack_weights_fp4(T)), K))
+    np.testing.assert_array_equal(acc, orc.gemm_s32(q, T))
+
+
+def test_gemm_fp6fp4_extremes(orc):
+    M, K, N = 40, 8192, 72
+    note("gemm fp6fp4 extremes")
+    q = np.full((M, K), 7, np.int8)
+    q[1::2] = -7
+    T = np.ones((N, K), np.int8)
+    T[::3] = -1
+    acc = to_host(B.gemm_fp6fp4_s32(to_dev(orc.pack_codes_fp6(q)), to_dev(orc.pack_weights_fp4(T)), K))
+    np.testing.assert_array_equal(acc, orc.gemm_s32(q, T))
+
+
+@pytest.mark.parametrize("name,M", [("tiny_exact", None), ("wo_1p3b", 64), ("wdown_7b", 24)])
+def test_forward_fp6fp4_matches_int4_path(orc, name, M):
+    wl = inputs.WORKLOADS[name]
+    note("forward fp6fp4", name, M)
+    x = wl.activations(M)
+    W = wl.weights()
+    T, alpha = orc.quantize_weights(W)
+    Wq, scale = B.quantize_weights(to_dev(W))
+    Wq4 = B.weights_to_fp4(Wq, wl.K)
+    xd = to_dev(x)
+    y6 = to_host(B.forward_fp6fp4(xd, Wq4, scale, wl.use_hadamard, norm=wl.norm))
+    y4 = to_host(B.forward(xd, Wq, scale, 4, wl.use_hadamard, norm=wl.norm))
+    np.testing.assert_array_equal(y6, y4)
+    y_o = orc.forward(x, T, alpha, 4, wl.use_hadamard, norm=wl.norm)
+    if name == "tiny_exact":
+        np.testing.assert_array_equal(y6, y_o)
+    else:
+        assert rel_fro(y6, y_o) <= 1e-3
+        assert_close_ulps(y6, y_o, 4, name)
+
+
+def test_forward_fp6fp4_full_size_sampled_rows(orc):
+    wl = inputs.WORKLOADS["wdown_7b"]
+    note("forward fp6fp4 full size")
+    x = wl.activations()
+    W = wl.weights()
+    T, alpha = orc.quantize_weights(W)
+    Wq, scale = B.quantize_weights(to_dev(W))
+    Wq4 = B.weights_to_fp4(Wq, wl.K)
+    y = to_host(B.forward_fp6fp4(to_dev(x), Wq4, scale, True, norm=True))
+    rows = np.unique(np.concatenate([np.random.default_rng(7).choice(wl.M, 30, replace=False), [0, wl.M - 1]]))
+    y_o = orc.forward(np.ascontiguousarray(x[rows]), T, alpha, 4, True, norm=True)
+    assert rel_fro(y[rows], y_o) <= 1e-3
+    assert_close_ulps(y[rows], y_o, 4, "wdown_7b fp6fp4")

@@ -81,3 +81,46 @@ def test_packing_round_trip(orc, abits):
     Wq = orc.pack_weights(T)
     assert Wq.shape == (9, 64)
     np.testing.assert_array_equal(orc.unpack_weights(Wq, 256), T)
+
+
+def _fp6_value(code: int) -> float:
+    """FP6 E2M3 value from its definition (independent of the oracle's encoder)."""
+    s = -1.0 if code & 0x20 else 1.0
+    e, m = (code >> 3) & 3, code & 7
+    return s * (m / 8.0 if e == 0 else 2.0 ** (e - 1) * (1 + m / 8.0))
+
+
+def _fp4_value(code: int) -> float:
+    s = -1.0 if code & 8 else 1.0
+    e, m = (code >> 1) & 3, code & 1
+    return s * (m / 2.0 if e == 0 else 2.0 ** (e - 1) * (1 + m / 2.0))
+
+
+def test_fp6_fp4_fixture(orc):
+    data = json.load(open(os.path.join(GOLDEN, "fp6_fp4_codes.json")))
+    for q, code in data["fp6_e2m3"].items():
+        assert _fp6_value(code) == int(q)
+        packed = orc.pack_codes_fp6(np.full((1, 4), int(q), np.int8))
+        assert packed[0, 0] & 63 == code
+    row = data["fp6_row"]
+    b = orc.pack_codes_fp6(np.array([row["q"]], np.int8))
+    assert b.tobytes().hex() == row["bytes_hex"]
+    for t, code in data["fp4_e2m1"].items():
+        assert _fp4_value(code) == int(t)
+    row = data["fp4_row"]
+    assert orc.pack_weights_fp4(np.array([row["t"]], np.int8)).tobytes().hex() == row["bytes_hex"]
+
+
+def test_fp6_round_trip_and_decoded_values(orc):
+    rng = np.random.default_rng(6)
+    q = rng.integers(-7, 8, size=(5, 256)).astype(np.int8)
+    b = orc.pack_codes_fp6(q)
+    assert b.shape == (5, 192)
+    np.testing.assert_array_equal(orc.unpack_codes_fp6(b, 256), q)
+    bits = np.unpackbits(b, axis=1, bitorder="little").reshape(5, 256, 6)
+    codes = (bits * (1 << np.arange(6))).sum(axis=2)
+    np.testing.assert_array_equal(np.vectorize(_fp6_value)(codes), q.astype(np.float64))
+    T = rng.integers(-1, 2, size=(3, 128)).astype(np.int8)
+    w = orc.pack_weights_fp4(T)
+    nib = np.stack([w & 15, w >> 4], axis=2).reshape(3, 128)
+    np.testing.assert_array_equal(np.vectorize(_fp4_value)(nib), T.astype(np.float64))
