@@ -41,8 +41,8 @@ def log(*a):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--workload", default="wdown_7b")
     p.add_argument("--abits", type=int, default=4)
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time of the CPU baseline")
@@ -63,6 +63,25 @@ def copy_calibration(mb: int) -> None:
         b.copy_(a)
     torch.cuda.synchronize()
     log(f"[bench] copied {mb} MiB three times")
+
+
+def measured_traffic(kernel: str):
+    """HBM-side bytes per launch of `kernel` from profiles/traffic.json (rocprofv3 FETCH_SIZE and
+    WRITE_SIZE per dispatch, each scaled by what the counter reads for a copy of known size),
+    or None if the kernel's sources have changed since the counters were taken."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    for e in json.load(open(path))["kernels"]:
+        if e["kernel"] != kernel:
+            continue
+        h = hashlib.sha256()
+        for f in e["sources"]:
+            h.update(open(os.path.join(ROOT, "bit_quantized_gemm_bitlinear_amd", "csrc", f), "rb").read())
+        return e["traffic_bytes"] if h.hexdigest() == e["sources_sha256"] else None
+    return None
 
 
 def act_bytes_per_token(K: int, abits: int, x_bytes: int) -> int:
@@ -175,6 +194,9 @@ def main():
     log(f"[bench] act-quant {t_act * 1e6:.1f} us ({act_gbs:.0f} GB/s), gemm {t_gemm * 1e6:.1f} us "
         f"({gemm_tops:.0f} TOPS), effective {eff_tops:.0f} TOPS")
 
+    gemm_kernel = f"k_gemm<{abits}, 256, 256, 2, 4, {256 if abits == 4 else 128}, 1>"
+    act_kernel = f"k_actquant_h<{K.bit_length() - 1}, {abits}, 1, 1>"
+
     # ---- CPU oracle baseline on a bounded sample of rows ----
     cpu = None
     if not args.no_cpu_baseline:
@@ -216,11 +238,15 @@ def main():
         "effective_pct_int8_peak": 100.0 * eff_tops / PEAK_INT8_TOPS,
         "kernels_us": {"actquant_fwht": t_act * 1e6, "gemm_dequant": t_gemm * 1e6},
         "roofline": {"bound": "mfma", "achieved": gemm_tops, "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
-                     "frac": gemm_tops / PEAK_INT8_TOPS, "traffic": None,
-                     "kernel": "k_gemm (ternary x INT%d, v_mfma_i32_16x16x64_i8)" % abits,
+                     "frac": gemm_tops / PEAK_INT8_TOPS,
+                     "traffic": measured_traffic(gemm_kernel) if wl.name == "wdown_7b" else None,
+                     "traffic_unit": "HBM-side bytes per launch (FETCH_SIZE x2.0 + WRITE_SIZE x1.0)",
+                     "kernel": "k_gemm (ternary x INT%d, v_mfma_i32_32x32x32_i8)" % abits,
                      "algorithmic": "2*M*N*K int8 ops per launch"},
         "roofline_actquant": {"bound": "hbm", "achieved": act_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                              "frac": act_gbs / PEAK_HBM_GBS, "traffic": None,
+                              "frac": act_gbs / PEAK_HBM_GBS,
+                              "traffic": measured_traffic(act_kernel) if wl.name == "wdown_7b" else None,
+                              "traffic_unit": "HBM-side bytes per launch (FETCH_SIZE x2.0 + WRITE_SIZE x1.0)",
                               "algorithmic": f"{act_bytes_per_token(K, abits, x_bytes)} B per token "
                                              "(read x, write packed codes + deq)"},
         "cpu_baseline": cpu,
@@ -229,8 +255,9 @@ def main():
 
 
 def bench_ffn(args, wl):
-    """The 7B-like a4 FFN block: RMSNorm -> INT4 BitLinear gate and up (one shared activation
-    quantisation) -> SwiGLU -> H-BitLinear down.  Reported separately from the headline."""
+    """The 7B-like a4 FFN block: RMSNorm -> BitLinear gate and up (one shared activation
+    quantisation, one fused GEMM whose epilogue writes h = silu(g) * u in bf16) -> H-BitLinear
+    down.  A step is one hbl_ffn_forward call.  Reported separately from the headline."""
     import numpy as np
     import torch
 
@@ -238,6 +265,7 @@ def bench_ffn(args, wl):
     from bit_quantized_gemm_bitlinear_amd import inputs
 
     M, hid, ffn = wl.M, wl.extra["hidden"], wl.extra["ffn"]
+    abits = 4
     dev = torch.device("cuda:0")
     log(f"[bench] workload {wl.name}: M={M} hidden={hid} ffn={ffn}")
     x_np = wl.activations()
@@ -246,70 +274,86 @@ def bench_ffn(args, wl):
     for name, (n, k, seed) in {"gate": (ffn, hid, wl.extra["seed_gate"]), "up": (ffn, hid, wl.extra["seed_up"]),
                                "down": (hid, ffn, wl.extra["seed_down"])}.items():
         Wq[name] = B.quantize_weights(torch.from_numpy(inputs.make_weights(n, k, seed=seed)).to(dev))
+    Wgu = B.interleave_gate_up(Wq["gate"][0], Wq["up"][0], hid)
+    sg, su = Wq["gate"][1], Wq["up"][1]
+    qd, sd = Wq["down"]
     torch.cuda.synchronize()
     L = B.lib()
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
-    codes = torch.empty((M, hid // 2), dtype=torch.uint8, device=dev)
-    deq = torch.empty(M, dtype=torch.float32, device=dev)
-    g = torch.empty((M, ffn), dtype=torch.float32, device=dev)
-    u = torch.empty_like(g)
-    h = torch.empty_like(g)
+    ht = B.HBL_BF16
+    ws = B.ffn_workspace(M, hid, ffn, abits, torch.bfloat16, dev)
     y = torch.empty((M, hid), dtype=torch.float32, device=dev)
-    ws = B.forward_workspace(M, ffn, 4, dev)
+    codes = torch.empty((M, hid * abits // 8), dtype=torch.uint8, device=dev)
+    deq = torch.empty(M, dtype=torch.float32, device=dev)
+    h = torch.empty((M, ffn), dtype=torch.bfloat16, device=dev)
+    ws_down = B.forward_workspace(M, ffn, abits, dev)
 
     def ok(st):
         if st != 0:
             raise RuntimeError(L.hbl_last_error().decode())
 
+    def step():
+        ok(L.hbl_ffn_forward(x.data_ptr(), B.HBL_BF16, Wgu.data_ptr(), sg.data_ptr(), su.data_ptr(), qd.data_ptr(),
+                             sd.data_ptr(), M, hid, ffn, abits, None, None, 1e-5, ht, y.data_ptr(), ws.data_ptr(),
+                             ws.numel(), sh))
+
     def q():
-        ok(L.hbl_quantize_activations(x.data_ptr(), B.HBL_BF16, M, hid, B.HBL_NORM_RMS, None, 1e-5, 4, 0,
+        ok(L.hbl_quantize_activations(x.data_ptr(), B.HBL_BF16, M, hid, B.HBL_NORM_RMS, None, 1e-5, abits, 0,
                                       codes.data_ptr(), deq.data_ptr(), sh))
 
-    def gate():
-        ok(L.hbl_gemm_dequant(codes.data_ptr(), deq.data_ptr(), Wq["gate"][0].data_ptr(), Wq["gate"][1].data_ptr(),
-                              M, hid, ffn, 4, g.data_ptr(), sh))
+    def gate_up():
+        ok(L.hbl_gate_up_swiglu(codes.data_ptr(), deq.data_ptr(), Wgu.data_ptr(), sg.data_ptr(), su.data_ptr(), M,
+                                hid, ffn, abits, ht, h.data_ptr(), sh))
 
-    def up():
-        ok(L.hbl_gemm_dequant(codes.data_ptr(), deq.data_ptr(), Wq["up"][0].data_ptr(), Wq["up"][1].data_ptr(),
-                              M, hid, ffn, 4, u.data_ptr(), sh))
+    def down_act():
+        ok(L.hbl_quantize_activations(h.data_ptr(), B.HBL_BF16, M, ffn, B.HBL_NORM_RMS, None, 1e-5, abits, 1,
+                                      ws_down.data_ptr(), ws_down[(M * ffn * abits // 8 + 255) // 256 * 256:]
+                                      .data_ptr(), sh))
 
-    def glu():
-        ok(L.hbl_swiglu(g.data_ptr(), u.data_ptr(), g.numel(), h.data_ptr(), sh))
+    def down_gemm():
+        off = (M * ffn * abits // 8 + 255) // 256 * 256
+        ok(L.hbl_gemm_dequant(ws_down.data_ptr(), ws_down[off:].data_ptr(), qd.data_ptr(), sd.data_ptr(), M, ffn,
+                              hid, abits, y.data_ptr(), sh))
 
-    def down():
-        ok(L.hbl_forward(h.data_ptr(), B.HBL_F32, Wq["down"][0].data_ptr(), Wq["down"][1].data_ptr(), M, ffn, hid, 4,
-                         1, B.HBL_NORM_RMS, None, 1e-5, y.data_ptr(), ws.data_ptr(), ws.numel(), sh))
-
-    parts = [("actquant_gate_up", q), ("gemm_gate", gate), ("gemm_up", up), ("swiglu", glu), ("down_forward", down)]
     for _ in range(args.warmup):
-        for _, f in parts:
-            f()
+        step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        for _, f in parts:
-            f()
+        step()
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
+    parts = [("actquant_gate_up", q), ("gemm_gate_up_swiglu", gate_up), ("actquant_down_fwht", down_act),
+             ("gemm_down", down_gemm)]
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)]
     sums = [0.0] * len(parts)
-    for _ in range(args.steps):
+    n_ev = max(args.steps, 10)
+    for _ in range(n_ev):
         ev[0].record(stream)
         for i, (_, f) in enumerate(parts):
             f()
             ev[i + 1].record(stream)
         torch.cuda.synchronize()
         for i in range(len(parts)):
-            sums[i] += ev[i].elapsed_time(ev[i + 1]) * 1e3 / args.steps
+            sums[i] += ev[i].elapsed_time(ev[i + 1]) * 1e3 / n_ev
     ops = 3 * 2.0 * M * hid * ffn
-    out = {"metric": "7B-like a4 FFN block tokens/s (RMSNorm, BitLinear gate/up, SwiGLU, H-BitLinear down)",
+    t_gu = sums[1] * 1e-6
+    gu_tops = 2 * 2.0 * M * hid * ffn / t_gu / 1e12
+    out = {"metric": "7B-like a4 FFN block tokens/s (RMSNorm, BitLinear gate/up + SwiGLU fused, H-BitLinear down)",
            "value": M * args.steps / el, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": el * 1e3 / args.steps, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": "i8", "data": "synthetic",
-           "config": {"workload": f"{wl.name}: {wl.description}", "M": M, "hidden": hid, "ffn": ffn, "abits": 4},
+           "config": {"workload": f"{wl.name}: {wl.description}", "M": M, "hidden": hid, "ffn": ffn, "abits": abits,
+                      "h_dtype": "bf16"},
            "effective_tops": ops / (el / args.steps) / 1e12,
-           "parts_us": {name: v for (name, _), v in zip(parts, sums)}}
+           "parts_us": {name: v for (name, _), v in zip(parts, sums)},
+           "roofline": {"bound": "mfma", "achieved": gu_tops, "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
+                        "frac": gu_tops / PEAK_INT8_TOPS,
+                        "traffic": measured_traffic("k_gemm<4, 256, 256, 2, 4, 256, 3>"),
+                        "traffic_unit": "HBM-side bytes per launch (FETCH_SIZE x2.0 + WRITE_SIZE x1.0)",
+                        "kernel": "k_gemm fused gate/up + SwiGLU epilogue (v_mfma_i32_32x32x32_i8)",
+                        "algorithmic": "2*M*(2*ffn)*hidden int8 ops per launch"}}
     log(f"[bench] ffn block {out['ms_per_step']:.3f} ms/step, parts " +
         ", ".join(f"{k} {v:.0f} us" for k, v in out["parts_us"].items()))
     print(json.dumps(out), flush=True)

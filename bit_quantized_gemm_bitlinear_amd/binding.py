@@ -57,6 +57,11 @@ def lib() -> ctypes.CDLL:
             "hbl_gemm_fp6fp4_s32": (I, [P, P, I64, I64, I64, P, P]),
             "hbl_gemm_fp6fp4_dequant": (I, [P, P, P, P, I64, I64, I64, P, P]),
             "hbl_forward_fp6fp4": (I, [P, I, P, P, I64, I64, I64, I, I, P, F, P, P, SZ, P]),
+            "hbl_packed_gate_up_bytes": (SZ, [I64, I64]),
+            "hbl_interleave_gate_up": (I, [P, P, I64, I64, P, P]),
+            "hbl_gate_up_swiglu": (I, [P, P, P, P, P, I64, I64, I64, I, I, P, P]),
+            "hbl_ffn_workspace_bytes": (SZ, [I64, I64, I64, I, I]),
+            "hbl_ffn_forward": (I, [P, I, P, P, P, P, P, I64, I64, I64, I, P, P, F, I, P, P, SZ, P]),
             "hbl_status_string": (ctypes.c_char_p, [I]),
             "hbl_last_error": (ctypes.c_char_p, []),
             "hbl_version": (I, []),
@@ -186,6 +191,68 @@ def swiglu(g, u, h=None):
         h = torch.empty_like(g)
     _check(lib().hbl_swiglu(_ptr(g), _ptr(u), g.numel(), _ptr(h), _stream()))
     return h
+
+
+# ---- FFN block ----------------------------------------------------------------------------
+
+def interleave_gate_up(Wq_gate, Wq_up, K: int):
+    """Two packed weights [F, K/4] -> Wgu [2F, K/4], interleaved in blocks of 32 rows."""
+    import torch
+
+    _dev(Wq_gate, Wq_up)
+    F = Wq_gate.shape[0]
+    Wgu = torch.empty((2 * F, K // 4), dtype=torch.uint8, device=Wq_gate.device)
+    _check(lib().hbl_interleave_gate_up(_ptr(Wq_gate), _ptr(Wq_up), F, K, _ptr(Wgu), _stream()))
+    return Wgu
+
+
+def _hdtype(h_dtype) -> int:
+    import torch
+
+    if h_dtype == torch.bfloat16:
+        return HBL_BF16
+    if h_dtype == torch.float32:
+        return HBL_F32
+    raise TypeError("h must be torch.bfloat16 or torch.float32")
+
+
+def gate_up_swiglu(codes, deq, Wgu, scale_gate, scale_up, K: int, abits: int, h_dtype=None, h=None):
+    """h [M, F] = silu(g) * u for the shared codes/deq and interleaved gate/up weights."""
+    import torch
+
+    _dev(codes, deq, Wgu, scale_gate, scale_up, h)
+    M, F = codes.shape[0], Wgu.shape[0] // 2
+    if h is None:
+        h = torch.empty((M, F), dtype=h_dtype or torch.float32, device=codes.device)
+    _check(lib().hbl_gate_up_swiglu(_ptr(codes), _ptr(deq), _ptr(Wgu), _ptr(scale_gate), _ptr(scale_up), M, K, F,
+                                    int(abits), _hdtype(h.dtype), _ptr(h), _stream()))
+    return h
+
+
+def ffn_workspace(M: int, D: int, F: int, abits: int, h_dtype, device="cuda"):
+    import torch
+
+    n = lib().hbl_ffn_workspace_bytes(M, D, F, abits, _hdtype(h_dtype))
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def ffn_forward(x, Wgu, scale_gate, scale_up, Wq_down, scale_down, abits: int = 4, h_dtype=None, gamma_in=None,
+                gamma_down=None, eps: float = 1e-5, y=None, ws=None):
+    """The FFN block x [M, D] -> y [M, D] fp32 (RMSNorm, gate/up, SwiGLU, H-BitLinear down)."""
+    import torch
+
+    _dev(x, Wgu, scale_gate, scale_up, Wq_down, scale_down, gamma_in, gamma_down, y, ws)
+    M, D = x.shape
+    F = Wgu.shape[0] // 2
+    h_dtype = h_dtype or torch.float32
+    if y is None:
+        y = torch.empty((M, D), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = ffn_workspace(M, D, F, abits, h_dtype, x.device)
+    _check(lib().hbl_ffn_forward(_ptr(x), _xdtype(x), _ptr(Wgu), _ptr(scale_gate), _ptr(scale_up), _ptr(Wq_down),
+                                 _ptr(scale_down), M, D, F, int(abits), _ptr(gamma_in), _ptr(gamma_down), float(eps),
+                                 _hdtype(h_dtype), _ptr(y), _ptr(ws), ws.numel(), _stream()))
+    return y
 
 
 # ---- FP6 x FP4 a4 path -------------------------------------------------------------------

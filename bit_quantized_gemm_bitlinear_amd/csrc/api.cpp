@@ -327,6 +327,116 @@ hbl_status hbl_forward_fp6fp4(const void* x, hbl_dtype xt, const uint8_t* Wq4, c
   }
 }
 
+size_t hbl_packed_gate_up_bytes(int64_t F, int64_t K) {
+  if (F < 32 || F % 32 != 0 || 2 * F > INT32_MAX || K < 64 || K % 64 != 0 || K > HBL_MAX_K) return 0;
+  return (size_t)(2 * F * (K / 4));
+}
+
+hbl_status hbl_interleave_gate_up(const uint8_t* Wq_gate, const uint8_t* Wq_up, int64_t F, int64_t K, uint8_t* Wgu,
+                                  void* stream) {
+  static const char* fn = "hbl_interleave_gate_up";
+  try {
+    if (F < 32 || F % 32 != 0 || 2 * F > INT32_MAX)
+      return fail(HBL_ERR_INVALID_ARG, fn, "F must be a positive multiple of 32 below 2^30");
+    HBL_TRY(check_shape(fn, 0, K, 2 * F, 4));
+    HBL_TRY(check_ptr(fn, Wq_gate, "Wq_gate", 16));
+    HBL_TRY(check_ptr(fn, Wq_up, "Wq_up", 16));
+    HBL_TRY(check_ptr(fn, Wgu, "Wgu", 16));
+    const size_t row = (size_t)(K / 4), blk = 32 * row;
+    const uintptr_t ob = reinterpret_cast<uintptr_t>(Wgu), oe = ob + 2 * (size_t)F * row;
+    for (const uint8_t* p : {Wq_gate, Wq_up}) {
+      const uintptr_t pb = reinterpret_cast<uintptr_t>(p), pe = pb + (size_t)F * row;
+      if (ob < pe && pb < oe) return fail(HBL_ERR_INVALID_ARG, fn, "Wgu overlaps an input");
+    }
+    hipStream_t s = (hipStream_t)stream;
+    // Block b of 32 gate rows goes to rows 64b..64b+31, the matching up rows to 64b+32..64b+63.
+    hipError_t e = hipMemcpy2DAsync(Wgu, 2 * blk, Wq_gate, blk, blk, (size_t)(F / 32), hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    e = hipMemcpy2DAsync(Wgu + blk, 2 * blk, Wq_up, blk, blk, (size_t)(F / 32), hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return HBL_OK;
+  } catch (...) {
+    return fail(HBL_ERR_HIP, fn, "unexpected C++ exception");
+  }
+}
+
+hbl_status hbl_gate_up_swiglu(const uint8_t* codes, const float* deq, const uint8_t* Wgu, const float* scale_gate,
+                              const float* scale_up, int64_t M, int64_t K, int64_t F, int abits, hbl_dtype ht, void* h,
+                              void* stream) {
+  static const char* fn = "hbl_gate_up_swiglu";
+  try {
+    if (F < 32 || F % 32 != 0 || 2 * F > INT32_MAX)
+      return fail(HBL_ERR_INVALID_ARG, fn, "F must be a positive multiple of 32 below 2^30");
+    HBL_TRY(check_shape(fn, M, K, 2 * F, abits));
+    if (ht != HBL_F32 && ht != HBL_BF16) return fail(HBL_ERR_INVALID_ARG, fn, "unknown h dtype");
+    HBL_TRY(check_ptr(fn, Wgu, "Wgu", 16));
+    HBL_TRY(check_ptr(fn, scale_gate, "scale_gate", 4));
+    HBL_TRY(check_ptr(fn, scale_up, "scale_up", 4));
+    if (M == 0) return HBL_OK;
+    HBL_TRY(check_ptr(fn, codes, "codes", 16));
+    HBL_TRY(check_ptr(fn, deq, "deq", 4));
+    HBL_TRY(check_ptr(fn, h, "h", 16));
+    hipError_t e = hbl::launch_gemm_swiglu(codes, deq, Wgu, scale_gate, scale_up, M, K, F, abits, ht == HBL_BF16, h,
+                                           (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return HBL_OK;
+  } catch (...) {
+    return fail(HBL_ERR_HIP, fn, "unexpected C++ exception");
+  }
+}
+
+size_t hbl_ffn_workspace_bytes(int64_t M, int64_t D, int64_t F, int abits, hbl_dtype ht) {
+  if (M < 0 || M > INT32_MAX || D < 64 || D % 64 != 0 || D > HBL_MAX_K || !pow2(F) || F < 64 ||
+      F > HBL_MAX_K_HADAMARD || (abits != 4 && abits != 8) || (ht != HBL_F32 && ht != HBL_BF16))
+    return 0;
+  const size_t hb = ht == HBL_BF16 ? 2 : 4;
+  return round256((size_t)(M * D * abits / 8)) + round256((size_t)M * sizeof(float)) + round256((size_t)(M * F) * hb) +
+         hbl_forward_workspace_bytes(M, F, abits);
+}
+
+hbl_status hbl_ffn_forward(const void* x, hbl_dtype xt, const uint8_t* Wgu, const float* scale_gate,
+                           const float* scale_up, const uint8_t* Wq_down, const float* scale_down, int64_t M, int64_t D,
+                           int64_t F, int abits, const float* gamma_in, const float* gamma_down, float norm_eps,
+                           hbl_dtype ht, float* y, void* ws, size_t ws_bytes, void* stream) {
+  static const char* fn = "hbl_ffn_forward";
+  try {
+    HBL_TRY(check_shape(fn, M, D, 2 * F, abits));
+    HBL_TRY(check_shape(fn, M, F, D, abits));
+    HBL_TRY(check_act(fn, xt, HBL_NORM_RMS, gamma_in, norm_eps, 0, D));
+    if (ht != HBL_F32 && ht != HBL_BF16) return fail(HBL_ERR_INVALID_ARG, fn, "unknown h dtype");
+    HBL_TRY(check_act(fn, ht, HBL_NORM_RMS, gamma_down, norm_eps, 1, F));
+    HBL_TRY(check_ptr(fn, Wgu, "Wgu", 16));
+    HBL_TRY(check_ptr(fn, scale_gate, "scale_gate", 4));
+    HBL_TRY(check_ptr(fn, scale_up, "scale_up", 4));
+    HBL_TRY(check_ptr(fn, Wq_down, "Wq_down", 16));
+    HBL_TRY(check_ptr(fn, scale_down, "scale_down", 4));
+    if (M == 0) return HBL_OK;
+    HBL_TRY(check_ptr(fn, x, "x", 16));
+    HBL_TRY(check_ptr(fn, y, "y", 16));
+    const size_t need = hbl_ffn_workspace_bytes(M, D, F, abits, ht);
+    if (ws == nullptr || ws_bytes < need)
+      return fail(HBL_ERR_WORKSPACE, fn, "workspace missing or smaller than hbl_ffn_workspace_bytes");
+    HBL_TRY(check_ptr(fn, ws, "ws", 256));
+    uint8_t* codes = static_cast<uint8_t*>(ws);
+    float* deq = reinterpret_cast<float*>(codes + round256((size_t)(M * D * abits / 8)));
+    uint8_t* h = reinterpret_cast<uint8_t*>(deq) + round256((size_t)M * sizeof(float));
+    uint8_t* codes2 = h + round256((size_t)(M * F) * (ht == HBL_BF16 ? 2 : 4));
+    float* deq2 = reinterpret_cast<float*>(codes2 + round256((size_t)(M * F * abits / 8)));
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = hbl::launch_actquant(x, (int)xt, M, D, (int)HBL_NORM_RMS, gamma_in, norm_eps, abits, 0, codes, deq, s);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    e = hbl::launch_gemm_swiglu(codes, deq, Wgu, scale_gate, scale_up, M, D, F, abits, ht == HBL_BF16, h, s);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    e = hbl::launch_actquant(h, (int)ht, M, F, (int)HBL_NORM_RMS, gamma_down, norm_eps, abits, 1, codes2, deq2, s);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    e = hbl::launch_gemm(codes2, deq2, Wq_down, scale_down, M, F, D, abits, nullptr, y, s);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return HBL_OK;
+  } catch (...) {
+    return fail(HBL_ERR_HIP, fn, "unexpected C++ exception");
+  }
+}
+
 hbl_status hbl_swiglu(const float* g, const float* u, int64_t n, float* h, void* stream) {
   static const char* fn = "hbl_swiglu";
   try {

@@ -12,6 +12,20 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// fp32 -> bf16 bit pattern, round to nearest even (NaN stays a quiet NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+// SwiGLU gate: silu(g) * u with silu(v) = v / (1 + exp(-v)), in fp32 with the device expf.
+// Shared by the standalone kernel and the fused GEMM epilogue so both give the same bits.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  const float sg = g / (1.0f + expf(-g));
+  return sg * u;
+}
+
 // Round half to even then convert (v_rndne_f32 + v_cvt_i32_f32).
 __device__ __forceinline__ int rne_int(float v) { return (int)__builtin_rintf(v); }
 

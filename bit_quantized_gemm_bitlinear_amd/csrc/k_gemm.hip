@@ -5,7 +5,7 @@
 // ternary weights and the result is rescaled by the activation and weight scales;
 // bitnet.cpp article: with weights in {-1, 0, 1} the product needs only additions.  On
 // MI355X the dense int8 MFMA path is faster than any add-only scheme, so the codes are
-// widened to int8 in registers and fed to v_mfma_i32_16x16x64_i8.
+// widened to int8 in registers and fed to v_mfma_i32_32x32x32_i8.
 //
 // Operand widening (exact; see the packed formats in hbl.h):
 //   INT4 codes: word w of 8 nibbles -> (w << 4) & 0xF0F0F0F0 and w & 0xF0F0F0F0 give int8
@@ -26,6 +26,12 @@
 // buffered, one barrier per stage), and each 32-deep step's fragments are read from LDS
 // one step ahead.  LDS rows are padded so the fragment reads hit distinct banks.  Small
 // problems use 128 x 128 tiles (4 waves) so that more CUs get work.
+//
+// Epilogues (MODE): 0 stores the int32 product, 1 the dequantised y.  2 and 3 are the fused
+// gate/up projection of the FFN block: B holds the gate and up weights interleaved in blocks
+// of 32 rows, so the two 32-column MFMA tiles of a wave hold g and u for the same outputs in
+// the same lanes; the epilogue dequantises both with their own weight scales and stores
+// h = silu(g) * u once (fp32 for 2, bf16 for 3) instead of writing g and u.
 #include <type_traits>
 
 #include "hbl_device.h"
@@ -67,8 +73,9 @@ struct Frag {
 template <int ABITS, int BM, int BN, int WR, int WC, int BK, int MODE>
 __global__ __launch_bounds__(64 * WR * WC) void k_gemm(const uint8_t* __restrict__ A, const float* __restrict__ deq,
                                                        const uint8_t* __restrict__ B,
-                                                       const float* __restrict__ w_scale, int M, int N, int K,
-                                                       int32_t* __restrict__ acc_out, float* __restrict__ y) {
+                                                       const float* __restrict__ w_scale,
+                                                       const float* __restrict__ w_scale_up, int M, int N, int K,
+                                                       int32_t* __restrict__ acc_out, void* __restrict__ out) {
   constexpr int NT = 64 * WR * WC;                  // threads per block
   constexpr int KS = BK / 32;                       // k-steps per stage
   constexpr int AB = BK * ABITS / 8;                // bytes of one A row per stage
@@ -84,6 +91,7 @@ __global__ __launch_bounds__(64 * WR * WC) void k_gemm(const uint8_t* __restrict
   constexpr int SHIFT = ABITS == 4 ? 10 : 6;
   static_assert(KS % 2 == 0, "stages hold an even number of k-steps");
   static_assert(ALD >= 1 && BLD >= 1 && ALD * NT == BM * ACH && BLD * NT == BN * BCH, "tile/thread mismatch");
+  static_assert(MODE < 2 || WN == 64, "the fused gate/up epilogue pairs a wave's two 32-column tiles");
 
   __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * AS];
   __shared__ __attribute__((aligned(16))) uint8_t sB[2][BN * BS];
@@ -224,6 +232,28 @@ __global__ __launch_bounds__(64 * WR * WC) void k_gemm(const uint8_t* __restrict
     if (has_next) fread(buf ^ 1, 0, f0);
   }
 
+  if constexpr (MODE >= 2) {
+    // Fused gate/up: B rows n0 + 64*wn + [0, 32) are gate rows and [32, 64) the up rows of
+    // the same 32 outputs h[:, n0/2 + 32*wn + (lane % 32)]; N here counts both (2F rows).
+    const float ag = w_scale[0], au = w_scale_up[0];
+    const int F = N / 2;
+    const int n = n0 / 2 + wn * 32 + (lane & 31);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = m0 + wm * WM + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (m >= M || n >= F) continue;
+        const float dm = deq[m];
+        const float g = __fmul_rn(__fmul_rn((float)(acc[i][0][v] >> SHIFT), dm), ag);
+        const float u = __fmul_rn(__fmul_rn((float)(acc[i][1][v] >> SHIFT), dm), au);
+        const float h = silu_mul(g, u);
+        if constexpr (MODE == 2) static_cast<float*>(out)[(int64_t)m * F + n] = h;
+        else static_cast<uint16_t*>(out)[(int64_t)m * F + n] = f32_to_bf16_rne(h);
+      }
+    }
+    return;
+  }
   float alpha = 0.0f;
   if constexpr (MODE == 1) alpha = w_scale[0];
 #pragma unroll
@@ -242,7 +272,7 @@ __global__ __launch_bounds__(64 * WR * WC) void k_gemm(const uint8_t* __restrict
         if constexpr (MODE == 0) {
           acc_out[(int64_t)m * N + n] = val;
         } else {
-          y[(int64_t)m * N + n] = __fmul_rn(__fmul_rn((float)val, dm), alpha);
+          static_cast<float*>(out)[(int64_t)m * N + n] = __fmul_rn(__fmul_rn((float)val, dm), alpha);
         }
       }
     }
@@ -250,11 +280,12 @@ __global__ __launch_bounds__(64 * WR * WC) void k_gemm(const uint8_t* __restrict
 }
 
 template <int ABITS, int BM, int BN, int WR, int WC, int BK, int MODE>
-hipError_t launch_cfg(const uint8_t* codes, const float* deq, const uint8_t* Wq, const float* w_scale, int64_t M,
-                      int64_t K, int64_t N, int32_t* acc, float* y, hipStream_t s) {
+hipError_t launch_cfg(const uint8_t* codes, const float* deq, const uint8_t* Wq, const float* w_scale,
+                      const float* w_scale_up, int64_t M, int64_t K, int64_t N, int32_t* acc, void* out,
+                      hipStream_t s) {
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   hipLaunchKernelGGL((k_gemm<ABITS, BM, BN, WR, WC, BK, MODE>), dim3((unsigned)tiles), dim3(64 * WR * WC), 0, s, codes,
-                     deq, Wq, w_scale, (int)M, (int)N, (int)K, acc, y);
+                     deq, Wq, w_scale, w_scale_up, (int)M, (int)N, (int)K, acc, out);
   return hipGetLastError();
 }
 
@@ -270,12 +301,12 @@ inline bool use_big_tiles(int64_t M, int64_t N) {
 }
 
 template <int ABITS, int MODE>
-hipError_t launch(const uint8_t* codes, const float* deq, const uint8_t* Wq, const float* w_scale, int64_t M,
-                  int64_t K, int64_t N, int32_t* acc, float* y, hipStream_t s) {
+hipError_t launch(const uint8_t* codes, const float* deq, const uint8_t* Wq, const float* w_scale,
+                  const float* w_scale_up, int64_t M, int64_t K, int64_t N, int32_t* acc, void* out, hipStream_t s) {
   constexpr int BKBIG = ABITS == 4 ? 256 : 128;  // INT8 A tiles are twice as wide in LDS
   if (use_big_tiles(M, N))
-    return launch_cfg<ABITS, 256, 256, 2, 4, BKBIG, MODE>(codes, deq, Wq, w_scale, M, K, N, acc, y, s);
-  return launch_cfg<ABITS, 128, 128, 2, 2, 128, MODE>(codes, deq, Wq, w_scale, M, K, N, acc, y, s);
+    return launch_cfg<ABITS, 256, 256, 2, 4, BKBIG, MODE>(codes, deq, Wq, w_scale, w_scale_up, M, K, N, acc, out, s);
+  return launch_cfg<ABITS, 128, 128, 2, 2, 128, MODE>(codes, deq, Wq, w_scale, w_scale_up, M, K, N, acc, out, s);
 }
 
 }  // namespace
@@ -284,10 +315,22 @@ hipError_t launch_gemm(const uint8_t* codes, const float* deq, const uint8_t* Wq
                        int64_t K, int64_t N, int abits, int32_t* acc, float* y, hipStream_t s) {
   if (M == 0) return hipSuccess;
   if (acc != nullptr)
-    return abits == 4 ? launch<4, 0>(codes, deq, Wq, w_scale, M, K, N, acc, y, s)
-                      : launch<8, 0>(codes, deq, Wq, w_scale, M, K, N, acc, y, s);
-  return abits == 4 ? launch<4, 1>(codes, deq, Wq, w_scale, M, K, N, acc, y, s)
-                    : launch<8, 1>(codes, deq, Wq, w_scale, M, K, N, acc, y, s);
+    return abits == 4 ? launch<4, 0>(codes, deq, Wq, w_scale, nullptr, M, K, N, acc, y, s)
+                      : launch<8, 0>(codes, deq, Wq, w_scale, nullptr, M, K, N, acc, y, s);
+  return abits == 4 ? launch<4, 1>(codes, deq, Wq, w_scale, nullptr, M, K, N, acc, y, s)
+                    : launch<8, 1>(codes, deq, Wq, w_scale, nullptr, M, K, N, acc, y, s);
+}
+
+hipError_t launch_gemm_swiglu(const uint8_t* codes, const float* deq, const uint8_t* Wgu, const float* scale_gate,
+                              const float* scale_up, int64_t M, int64_t K, int64_t F, int abits, int h_bf16, void* h,
+                              hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  const int64_t N = 2 * F;
+  if (abits == 4)
+    return h_bf16 ? launch<4, 3>(codes, deq, Wgu, scale_gate, scale_up, M, K, N, nullptr, h, s)
+                  : launch<4, 2>(codes, deq, Wgu, scale_gate, scale_up, M, K, N, nullptr, h, s);
+  return h_bf16 ? launch<8, 3>(codes, deq, Wgu, scale_gate, scale_up, M, K, N, nullptr, h, s)
+                : launch<8, 2>(codes, deq, Wgu, scale_gate, scale_up, M, K, N, nullptr, h, s);
 }
 
 }  // namespace hbl

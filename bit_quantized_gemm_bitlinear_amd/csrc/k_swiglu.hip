@@ -10,11 +10,6 @@
 namespace hbl {
 namespace {
 
-__device__ __forceinline__ float silu_mul(float g, float u) {
-  const float sg = g / (1.0f + expf(-g));
-  return sg * u;
-}
-
 __global__ __launch_bounds__(256) void k_swiglu(const float* __restrict__ g, const float* __restrict__ u,
                                                 int64_t n, float* __restrict__ h) {
   const int64_t n4 = n / 4;

@@ -170,6 +170,40 @@ hbl_status hbl_forward(const void* x, hbl_dtype xt, const uint8_t* Wq, const flo
  *  g, u, h: n fp32 each; h may alias neither g nor u.  n >= 0. */
 hbl_status hbl_swiglu(const float* g, const float* u, int64_t n, float* h, void* stream);
 
+/* ---- FFN block ---------------------------------------------------------------------------
+ * The LLaMA-like FFN of BitNet v2 (write-up section "BitNet v2：原生4位激活": RMSNorm,
+ * SwishGLU, no biases; section H-BitLinear模塊: only the down projection takes the Hadamard
+ * transform, gate and up are plain BitLinear):
+ *     codes, deq = quantize_activations(x, RMS with gamma_in, no transform)   (shared)
+ *     g = gemm_dequant(codes, deq, Wq_gate, scale_gate)                     [M, F]
+ *     u = gemm_dequant(codes, deq, Wq_up,   scale_up)                       [M, F]
+ *     h = silu(g) * u                      (as hbl_swiglu; rounded to bf16 if ht = HBL_BF16)
+ *     y = forward(h, Wq_down, scale_down, RMS with gamma_down, Hadamard over F)   [M, D]
+ * Gate and up run as one GEMM over their interleaved weights whose epilogue writes only h;
+ * g and u never reach memory.  Every value equals the unfused sequence of calls bit for bit. */
+
+/* Wgu — the gate and up weights (each in the Wq format, F rows of K/4 bytes) interleaved in
+ * blocks of 32 rows: rows 64b .. 64b+31 of Wgu are gate rows 32b .. 32b+31, rows 64b+32 ..
+ * 64b+63 the up rows 32b .. 32b+31.  F % 32 == 0.  Size 2*F*K/4 bytes (0 if invalid). */
+size_t hbl_packed_gate_up_bytes(int64_t F, int64_t K);
+/* Builds Wgu from two packed weights (two strided device copies on the stream); no overlap. */
+hbl_status hbl_interleave_gate_up(const uint8_t* Wq_gate, const uint8_t* Wq_up, int64_t F, int64_t K, uint8_t* Wgu,
+                                  void* stream);
+/* h [M, F] (fp32 or bf16 by ht) = silu(g) * u with g, u as hbl_gemm_dequant of the shared
+ * codes [M, K*abits/8] / deq [M] with the gate (scale_gate) and up (scale_up) halves of Wgu. */
+hbl_status hbl_gate_up_swiglu(const uint8_t* codes, const float* deq, const uint8_t* Wgu, const float* scale_gate,
+                              const float* scale_up, int64_t M, int64_t K, int64_t F, int abits, hbl_dtype ht, void* h,
+                              void* stream);
+/* Workspace of hbl_ffn_forward: input codes + deq, h, and the down projection's codes + deq. */
+size_t hbl_ffn_workspace_bytes(int64_t M, int64_t D, int64_t F, int abits, hbl_dtype ht);
+/* The whole block: x [M, D] (xt) -> y [M, D] fp32.  D % 64 == 0; F a power of two in
+ * [64, HBL_MAX_K_HADAMARD]; gamma_in [D] / gamma_down [F] or NULL for unit gamma; ht is the
+ * storage type of h; the same abits for both quantisations. */
+hbl_status hbl_ffn_forward(const void* x, hbl_dtype xt, const uint8_t* Wgu, const float* scale_gate,
+                           const float* scale_up, const uint8_t* Wq_down, const float* scale_down, int64_t M, int64_t D,
+                           int64_t F, int abits, const float* gamma_in, const float* gamma_down, float norm_eps,
+                           hbl_dtype ht, float* y, void* ws, size_t ws_bytes, void* stream);
+
 /* ---- FP6 x FP4 a4 path ----------------------------------------------------------------
  * The same layer with the a4 codes stored as FP6 and the weights as FP4 (formats above);
  * outputs are bit-identical to the INT4 / 2-bit calls.  Written for the 4-bit matrix

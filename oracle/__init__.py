@@ -14,6 +14,7 @@ from .oracle import (  # noqa: F401
     dense_reference,
     dequant,
     forward,
+    ffn_forward,
     fwht_f32,
     fwht_f64,
     gemm_s32,
@@ -26,6 +27,7 @@ from .oracle import (  # noqa: F401
     pack_weights,
     quantize_activations,
     quantize_weights,
+    round_bf16,
     set_num_threads,
     swiglu,
     unpack_codes,

@@ -272,6 +272,36 @@ void orc_swiglu(const float* g, const float* u, int64_t n, float* h) {
   }
 }
 
+/* fp32 -> bfloat16, round to nearest with ties to even.  bfloat16 keeps the sign, the
+ * 8-bit exponent and the top 7 fraction bits of binary32, so it has 8 significant bits and
+ * the same exponent range: a value of magnitude in [2^e, 2^(e+1)) is rounded to a multiple
+ * of 2^(e-7), and values below 2^-126 to multiples of 2^-133 (the subnormal spacing).  The
+ * rounded value is exact in binary32; its top 16 bits are the bfloat16 pattern.  Results of
+ * magnitude 2^128 or more overflow to infinity. */
+void orc_round_bf16(const float* in, int64_t n, uint16_t* out) {
+  for (int64_t i = 0; i < n; ++i) {
+    const float f = in[i];
+    float r;
+    if (isnan(f)) {
+      out[i] = (uint16_t)(signbit(f) ? 0xFFC0u : 0x7FC0u);
+      continue;
+    } else if (isinf(f) || f == 0.0f) {
+      r = f;
+    } else {
+      int e;
+      frexp((double)f, &e); /* |f| in [2^(e-1), 2^e) */
+      int qexp = (e - 1) - 7;
+      if (qexp < -133) qexp = -133;
+      const double q = ldexp(1.0, qexp);
+      const double v = rint((double)f / q) * q; /* exact scaling, one rounding (ties to even) */
+      r = fabs(v) >= 0x1p128 ? (v > 0 ? INFINITY : -INFINITY) : (float)v;
+    }
+    uint32_t bits;
+    memcpy(&bits, &r, sizeof bits);
+    out[i] = (uint16_t)(bits >> 16);
+  }
+}
+
 /* ------------------------------------------------------------------------------------
  * Packed formats (the header of the C ABI documents them; not given by the pages).
  * ------------------------------------------------------------------------------------ */

@@ -67,6 +67,7 @@ def _load():
         lib.orc_forward.argtypes = [P, I, P, Fl, I64, I64, I64, I, I, I, P, Fl, P, P, P, P]
         lib.orc_forward.restype = I
         lib.orc_swiglu.argtypes = [P, P, I64, P]
+        lib.orc_round_bf16.argtypes = [P, I64, P]
         lib.orc_pack_weights.argtypes = [P, I64, I64, P]
         lib.orc_pack_weights.restype = I
         lib.orc_unpack_weights.argtypes = [P, I64, I64, P]
@@ -201,6 +202,33 @@ def swiglu(g, u) -> np.ndarray:
     h = np.empty_like(g)
     _load().orc_swiglu(_p(g), _p(u), g.size, _p(h))
     return h
+
+
+def round_bf16(a) -> np.ndarray:
+    """fp32 -> bf16 bit patterns (uint16), round to nearest even."""
+    a = _c(a, np.float32)
+    out = np.empty(a.shape, np.uint16)
+    _load().orc_round_bf16(_p(a), a.size, _p(out))
+    return out
+
+
+def ffn_forward(x, Tg, ag: float, Tu, au: float, Td, ad: float, abits: int = 4, h_bf16: bool = True,
+                gamma_in=None, gamma_down=None, eps: float = 1e-5, intermediates: bool = False):
+    """The BitNet v2 FFN block (write-up section "BitNet v2：原生4位激活": RMSNorm, SwishGLU,
+    no biases; only the down projection is an H-BitLinear):
+
+        g = BitLinear_gate(RMSNorm(x)), u = BitLinear_up(RMSNorm(x))   (no transform)
+        h = silu(g) * u                                                  (fp32; bf16 if h_bf16)
+        y = H-BitLinear_down(h)                                          (RMSNorm, FWHT over F)
+
+    Returns y, or (y, h) with intermediates."""
+    g = forward(x, Tg, ag, abits, False, norm=True, gamma=gamma_in, eps=eps)
+    u = forward(x, Tu, au, abits, False, norm=True, gamma=gamma_in, eps=eps)
+    h = swiglu(g, u)
+    if h_bf16:
+        h = round_bf16(h)
+    y = forward(h, Td, ad, abits, True, norm=True, gamma=gamma_down, eps=eps)
+    return (y, h) if intermediates else y
 
 
 def pack_weights(T) -> np.ndarray:

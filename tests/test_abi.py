@@ -167,3 +167,64 @@ def test_last_error_is_thread_local(L):
     t.join()
     assert seen[0].startswith("hbl_quantize_activations")
     assert "abits" in L.hbl_last_error().decode()
+
+
+def test_fp6fp4_rejects(L):
+    assert L.hbl_packed_weight_fp4_bytes(8, 256) == 8 * 128
+    assert L.hbl_packed_act_fp6_bytes(8, 256) == 8 * 192
+    assert L.hbl_packed_act_fp6_bytes(8, 100) == 0
+    assert L.hbl_weights_to_fp4(FAKE, 0, 256, FAKE, S) == B.HBL_ERR_INVALID_ARG
+    assert L.hbl_weights_to_fp4(FAKE, 8, 256, FAKE_MIS, S) == B.HBL_ERR_INVALID_ARG
+    q6 = L.hbl_quantize_activations_fp6
+    assert q6(FAKE, 1, 4, 192, 0, None, 1e-5, 1, FAKE, FAKE, S) == B.HBL_ERR_UNSUPPORTED
+    assert q6(FAKE, 1, 4, 256, 0, None, 1e-5, 1, None, FAKE, S) == B.HBL_ERR_INVALID_ARG
+    assert q6(None, 1, 0, 256, 0, None, 1e-5, 1, None, None, S) == B.HBL_OK
+    assert L.hbl_gemm_fp6fp4_s32(FAKE, FAKE, 4, 200, 8, FAKE, S) == B.HBL_ERR_INVALID_ARG
+    assert L.hbl_gemm_fp6fp4_dequant(FAKE, FAKE, FAKE, None, 4, 256, 8, FAKE, S) == B.HBL_ERR_INVALID_ARG
+    f = L.hbl_forward_fp6fp4
+    assert f(FAKE, 1, FAKE, FAKE, 4, 256, 8, 1, 1, None, 1e-5, FAKE, FAKE, 100, S) == B.HBL_ERR_WORKSPACE
+    assert f(FAKE, 1, FAKE, FAKE, 4, 256, 8, 2, 1, None, 1e-5, FAKE, FAKE, 1 << 20, S) == B.HBL_ERR_INVALID_ARG
+
+
+def test_ffn_size_helpers(L):
+    assert L.hbl_packed_gate_up_bytes(16384, 4096) == 2 * 16384 * 1024
+    assert L.hbl_packed_gate_up_bytes(48, 256) == 0                     # F % 32 != 0
+    ws = L.hbl_ffn_workspace_bytes(8192, 4096, 16384, 4, B.HBL_BF16)
+    assert ws >= 8192 * 2048 + 8192 * 4 + 8192 * 16384 * 2 + 8192 * 8192 + 8192 * 4 and ws % 256 == 0
+    assert L.hbl_ffn_workspace_bytes(8, 4096, 12288, 4, B.HBL_BF16) == 0  # F not a power of two
+
+
+def test_gate_up_rejects(L):
+    il = L.hbl_interleave_gate_up
+    assert il(FAKE, FAKE + (1 << 24), 48, 256, FAKE + (1 << 25), S) == B.HBL_ERR_INVALID_ARG
+    assert il(FAKE, FAKE + (1 << 24), 64, 256, FAKE + 1024, S) == B.HBL_ERR_INVALID_ARG    # Wgu overlaps gate
+    assert il(FAKE, None, 64, 256, FAKE + (1 << 25), S) == B.HBL_ERR_INVALID_ARG
+    g = L.hbl_gate_up_swiglu
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 256, 40, 4, 1, FAKE, S) == B.HBL_ERR_INVALID_ARG   # F % 32
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 256, 64, 4, 5, FAKE, S) == B.HBL_ERR_INVALID_ARG   # h dtype
+    assert g(FAKE, FAKE, FAKE, None, FAKE, 4, 256, 64, 4, 1, FAKE, S) == B.HBL_ERR_INVALID_ARG
+    assert g(FAKE, FAKE, FAKE, FAKE, None, 4, 256, 64, 4, 1, FAKE, S) == B.HBL_ERR_INVALID_ARG
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 256, 64, 4, 1, FAKE_MIS, S) == B.HBL_ERR_INVALID_ARG
+    assert g(None, None, FAKE, FAKE, FAKE, 0, 256, 64, 4, 1, None, S) == B.HBL_OK
+
+
+def _ffn(L, x=FAKE, xt=B.HBL_BF16, M=16, D=256, F=512, abits=4, ht=B.HBL_BF16, y=FAKE, ws=FAKE, wsb=1 << 30,
+         gi=None, gd=None, eps=1e-5):
+    return L.hbl_ffn_forward(x, xt, FAKE, FAKE, FAKE, FAKE, FAKE, M, D, F, abits, gi, gd, eps, ht, y, ws, wsb, S)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(F=768), B.HBL_ERR_UNSUPPORTED),             # the down projection's transform needs a power of two
+    (dict(F=65536), B.HBL_ERR_UNSUPPORTED),
+    (dict(D=200), B.HBL_ERR_INVALID_ARG),
+    (dict(abits=6), B.HBL_ERR_INVALID_ARG),
+    (dict(ht=9), B.HBL_ERR_INVALID_ARG),
+    (dict(xt=9), B.HBL_ERR_INVALID_ARG),
+    (dict(gd=FAKE_MIS), B.HBL_ERR_INVALID_ARG),
+    (dict(y=None), B.HBL_ERR_INVALID_ARG),
+    (dict(wsb=1000), B.HBL_ERR_WORKSPACE),
+    (dict(ws=FAKE + 64), B.HBL_ERR_INVALID_ARG),
+    (dict(M=0, x=None, y=None, ws=None), B.HBL_OK),
+])
+def test_ffn_forward_rejects(L, kw, status):
+    assert _ffn(L, **kw) == status
