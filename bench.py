@@ -110,6 +110,8 @@ def main():
     wl = inputs.WORKLOADS[args.workload]
     if wl.name == "ffn_7b":
         return bench_ffn(args, wl)
+    if wl.name == "decode_7b":
+        return bench_decode(args, wl)
     abits = args.abits
     M, K, N = wl.M, wl.K, wl.N
     dev = torch.device("cuda:0")
@@ -356,6 +358,85 @@ def bench_ffn(args, wl):
                         "algorithmic": "2*M*(2*ffn)*hidden int8 ops per launch"}}
     log(f"[bench] ffn block {out['ms_per_step']:.3f} ms/step, parts " +
         ", ".join(f"{k} {v:.0f} us" for k, v in out["parts_us"].items()))
+    print(json.dumps(out), flush=True)
+
+
+def bench_decode(args, wl):
+    """H-BitLinear a4 forward in the decode regime (M = 1..64 token rows per step) at the
+    7B-like Wdown shape.  Each step uses the next of several copies of the packed weights, so
+    the 16.8 MB weight read comes from HBM rather than the 256 MB Infinity Cache, as it would
+    for a model whose layers do not fit there.  The headline line is M = 16; the other batch
+    sizes are listed under "per_batch"."""
+    import numpy as np
+    import torch
+
+    from bit_quantized_gemm_bitlinear_amd import binding as B
+
+    K, N = wl.K, wl.N
+    dev = torch.device("cuda:0")
+    batches = wl.extra["batches"]
+    copies = wl.extra["weight_copies"]
+    x_np = wl.activations(max(batches))
+    x_all = torch.from_numpy(x_np.view(np.int16)).to(dev).view(torch.bfloat16)
+    Wq0, scale = B.quantize_weights(torch.from_numpy(wl.weights()).to(dev))
+    Wqs = [Wq0.clone() for _ in range(copies)]
+    L = B.lib()
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    ws = B.forward_workspace(max(batches), K, 4, dev)
+    y = torch.empty((max(batches), N), dtype=torch.float32, device=dev)
+    steps = max(args.steps, 100)
+    per = {}
+    for M in batches:
+        x = x_all[:M]
+        codes = ws[:M * K // 2]
+        deq = ws[(M * K // 2 + 255) // 256 * 256:][:4 * M].view(torch.float32)
+
+        def ok(st):
+            if st != 0:
+                raise RuntimeError(L.hbl_last_error().decode())
+
+        def step(i):
+            ok(L.hbl_forward(x.data_ptr(), B.HBL_BF16, Wqs[i % copies].data_ptr(), scale.data_ptr(), M, K, N, 4, 1,
+                             B.HBL_NORM_RMS, None, 1e-5, y.data_ptr(), ws.data_ptr(), ws.numel(), sh))
+
+        for i in range(max(args.warmup, copies)):
+            step(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step(i)
+        torch.cuda.synchronize()
+        el = (time.perf_counter() - t0) / steps
+        # per-kernel durations with HIP events on the launch stream
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        for i in range(steps):
+            ev[i][0].record(stream)
+            ok(L.hbl_quantize_activations(x.data_ptr(), B.HBL_BF16, M, K, B.HBL_NORM_RMS, None, 1e-5, 4, 1,
+                                          codes.data_ptr(), deq.data_ptr(), sh))
+            ev[i][1].record(stream)
+            ok(L.hbl_gemm_dequant(codes.data_ptr(), deq.data_ptr(), Wqs[i % copies].data_ptr(), scale.data_ptr(), M,
+                                  K, N, 4, y.data_ptr(), sh))
+            ev[i][2].record(stream)
+        torch.cuda.synchronize()
+        t_act = sum(e[0].elapsed_time(e[1]) for e in ev) / steps * 1e-3
+        t_gemv = sum(e[1].elapsed_time(e[2]) for e in ev) / steps * 1e-3
+        gemv_bytes = N * K // 4 + M * K // 2 + 4 * M + 4 + 4 * M * N
+        per[M] = {"us_per_step": el * 1e6, "tokens_per_s": M / el, "actquant_us": t_act * 1e6,
+                  "gemv_us": t_gemv * 1e6, "gemv_bytes": gemv_bytes, "gemv_gbs": gemv_bytes / t_gemv / 1e9}
+        log(f"[bench] decode M={M}: {el * 1e6:.2f} us/step, act {t_act * 1e6:.2f} us, gemv {t_gemv * 1e6:.2f} us "
+            f"({gemv_bytes / t_gemv / 1e9:.0f} GB/s)")
+    head = per[wl.M]
+    out = {"metric": "H-BitLinear a4 decode tokens/s, 7B-like Wdown (weights streamed from HBM)",
+           "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": args.warmup,
+           "ms_per_step": head["us_per_step"] * 1e-3, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "i8", "data": "synthetic",
+           "config": {"workload": f"{wl.name}: {wl.description}", "M": wl.M, "K": K, "N": N, "abits": 4},
+           "per_batch": {str(k): v for k, v in per.items()},
+           "roofline": {"bound": "hbm", "achieved": head["gemv_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": head["gemv_gbs"] / PEAK_HBM_GBS, "traffic": None,
+                        "kernel": "k_gemv (decode GEMM, v_mfma_i32_16x16x64_i8)",
+                        "algorithmic": "N*K/4 weight bytes + M*K/2 code bytes + 4*M*N output bytes per launch"}}
     print(json.dumps(out), flush=True)
 
 

@@ -21,6 +21,11 @@ hipError_t launch_actquant(const void* x, int xt, int64_t M, int64_t K, int norm
 hipError_t launch_gemm(const uint8_t* codes, const float* deq, const uint8_t* Wq, const float* w_scale,
                        int64_t M, int64_t K, int64_t N, int abits, int32_t* acc, float* y, hipStream_t s);
 
+// Decode-regime GEMM for M <= GEMV_MAX_M token rows (k_gemv.hip); launch_gemm dispatches to it.
+constexpr int64_t GEMV_MAX_M = 64;
+hipError_t launch_gemv(const uint8_t* codes, const float* deq, const uint8_t* Wq, const float* w_scale,
+                       int64_t M, int64_t K, int64_t N, int abits, int32_t* acc, float* y, hipStream_t s);
+
 // Fused FFN gate/up projection (k_gemm.hip): Wgu holds 2F rows, gate and up interleaved in
 // blocks of 32; h [M, F] = silu(g) * u stored as fp32 (h_bf16 = 0) or bf16 (h_bf16 = 1).
 hipError_t launch_gemm_swiglu(const uint8_t* codes, const float* deq, const uint8_t* Wgu, const float* scale_gate,

@@ -314,6 +314,7 @@ hipError_t launch(const uint8_t* codes, const float* deq, const uint8_t* Wq, con
 hipError_t launch_gemm(const uint8_t* codes, const float* deq, const uint8_t* Wq, const float* w_scale, int64_t M,
                        int64_t K, int64_t N, int abits, int32_t* acc, float* y, hipStream_t s) {
   if (M == 0) return hipSuccess;
+  if (M <= GEMV_MAX_M) return launch_gemv(codes, deq, Wq, w_scale, M, K, N, abits, acc, y, s);
   if (acc != nullptr)
     return abits == 4 ? launch<4, 0>(codes, deq, Wq, w_scale, nullptr, M, K, N, acc, y, s)
                       : launch<8, 0>(codes, deq, Wq, w_scale, nullptr, M, K, N, acc, y, s);

@@ -136,4 +136,10 @@ WORKLOADS = {
                     "H-BitLinear down",
         extra={"hidden": 4096, "ffn": 16384, "seed_gate": SEED_W, "seed_up": SEED_W_UP,
                "seed_down": SEED_W_DOWN}),
+    "decode_7b": Workload(
+        "decode_7b", 16, 16384, 4096, (4,), True, True, "mixture", 0.01, 50.0,
+        description="7B-like FFN Wdown in the decode regime: 16 token rows per step (also 1, 4 and 64), "
+                    "K=16384, N=4096, the wdown_7b activation recipe, a fresh weight matrix per step "
+                    "(48 copies rotated, 805 MB, so weights stream from HBM)",
+        extra={"batches": (1, 4, 16, 64), "weight_copies": 48}),
 }

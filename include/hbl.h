@@ -145,6 +145,10 @@ hbl_status hbl_quantize_activations(const void* x, hbl_dtype xt, int64_t M, int6
                                     const float* gamma, float norm_eps, int abits, int use_hadamard,
                                     uint8_t* codes, float* deq, void* stream);
 
+/* GEMM kernels: M <= 64 token rows (the decode regime) run a kernel that streams every weight
+ * byte once and splits K over the waves of a block; larger M runs the tiled kernel.  Both
+ * compute the exact integer product, so the choice never changes a result. */
+
 /* hbl_gemm_s32 — the integer product acc = q . t^T (exact), for inspection and tests.
  *  codes [M, K*abits/8], Wq [N, K/4], acc [M, N] int32 row-major.  N >= 1. */
 hbl_status hbl_gemm_s32(const uint8_t* codes, const uint8_t* Wq, int64_t M, int64_t K, int64_t N,

@@ -1,0 +1,94 @@
+"""Parity of the decode-regime GEMM (M <= 64 token rows, k_gemv) against the oracle.
+
+hbl_gemm_s32 / hbl_gemm_dequant / hbl_forward run the decode kernel for M <= 64 and the
+tiled kernel above; both compute the exact integer product, so the int32 results must equal
+the oracle's bit for bit, and the first 64 rows of an M = 65 call (tiled kernel) must equal
+an M = 64 call (decode kernel) on the same data.
+"""
+import numpy as np
+import pytest
+
+from bit_quantized_gemm_bitlinear_amd import binding as B
+from bit_quantized_gemm_bitlinear_amd import inputs
+from tests.gpu_util import assert_close_ulps, note, rel_fro, to_dev, to_host, torch_mod
+
+pytestmark = pytest.mark.gpu
+
+
+def _rand(M, K, N, abits, seed):
+    rng = np.random.default_rng(seed)
+    Qb = 7 if abits == 4 else 127
+    q = rng.integers(-Qb - 1, Qb + 1, size=(M, K)).astype(np.int8)
+    T = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+    return q, T
+
+
+# M across the 16-row token tiles (1, 2 and 4 tiles, ragged), K with partial 256-deep groups
+# and fewer groups than waves, N ragged against the 16-column block.
+CASES = [(1, 64, 1), (1, 16384, 4096), (2, 192, 17), (15, 320, 33), (16, 1088, 300), (17, 2048, 15),
+         (31, 576, 64), (33, 4096, 130), (48, 16384, 100), (63, 8192, 257), (64, 1024, 4100)]
+
+
+@pytest.mark.parametrize("abits", [4, 8])
+@pytest.mark.parametrize("M,K,N", CASES)
+def test_gemv_s32_bit_exact(orc, M, K, N, abits):
+    note("gemv s32", M, K, N, abits)
+    q, T = _rand(M, K, N, abits, M * 131 + K + N)
+    acc = to_host(B.gemm_s32(to_dev(orc.pack_codes(q, abits)), to_dev(orc.pack_weights(T)), K, abits))
+    np.testing.assert_array_equal(acc, orc.gemm_s32(q, T))
+
+
+@pytest.mark.parametrize("abits", [4, 8])
+def test_gemv_extremes(orc, abits):
+    M, K, N = 64, 16384, 48
+    for qv in ([-8, 7] if abits == 4 else [-128, 127]):
+        note("gemv extremes", abits, qv)
+        q = np.full((M, K), qv, np.int8)
+        T = np.ones((N, K), np.int8)
+        T[1::2] = -1
+        acc = to_host(B.gemm_s32(to_dev(orc.pack_codes(q, abits)), to_dev(orc.pack_weights(T)), K, abits))
+        np.testing.assert_array_equal(acc, orc.gemm_s32(q, T))
+
+
+@pytest.mark.parametrize("abits", [4, 8])
+def test_gemv_dequant_bit_exact(orc, abits):
+    M, K, N = 40, 2112, 333
+    note("gemv dequant", M, K, N, abits)
+    q, T = _rand(M, K, N, abits, 5)
+    rng = np.random.default_rng(6)
+    deq = rng.uniform(1e-4, 3.0, M).astype(np.float32)
+    alpha = np.float32(0.0123)
+    torch = torch_mod()
+    y = B.gemm_dequant(to_dev(orc.pack_codes(q, abits)), to_dev(deq), to_dev(orc.pack_weights(T)),
+                       torch.tensor([alpha], device="cuda"), K, abits)
+    np.testing.assert_array_equal(to_host(y), orc.dequant(orc.gemm_s32(q, T), deq, float(alpha)))
+
+
+@pytest.mark.parametrize("abits", [4, 8])
+def test_decode_and_tiled_kernels_agree(orc, abits):
+    K, N = 4096, 520
+    note("gemv vs tiled", K, N, abits)
+    q, T = _rand(65, K, N, abits, 77)
+    codes = to_dev(orc.pack_codes(q, abits))
+    Wq = to_dev(orc.pack_weights(T))
+    tiled = to_host(B.gemm_s32(codes, Wq, K, abits))          # M = 65: tiled kernel
+    decode = to_host(B.gemm_s32(codes[:64].contiguous(), Wq, K, abits))
+    np.testing.assert_array_equal(decode, tiled[:64])
+
+
+@pytest.mark.parametrize("M", [1, 4, 16, 64])
+def test_decode_forward_7b_wdown(orc, M):
+    """The whole H-BitLinear forward at the 7B Wdown shape with decode batch sizes."""
+    wl = inputs.WORKLOADS["wdown_7b"]
+    note("decode forward", M)
+    x = wl.activations(M)
+    W = inputs.make_weights(wl.N, wl.K)
+    T, alpha = orc.quantize_weights(W)
+    Wq, scale = B.quantize_weights(to_dev(W))
+    ws = B.forward_workspace(M, wl.K, 4)
+    y = to_host(B.forward(to_dev(x), Wq, scale, 4, True, norm=True, ws=ws))
+    y_o, q_o, _, _ = orc.forward(x, T, alpha, 4, True, norm=True, intermediates=True)
+    codes = to_host(ws[:M * wl.K // 2]).reshape(M, wl.K // 2)
+    np.testing.assert_array_equal(codes, orc.pack_codes(q_o, 4))
+    assert rel_fro(y, y_o) <= 1e-3
+    assert_close_ulps(y, y_o, 4, "decode forward")
