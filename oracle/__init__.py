@@ -20,16 +20,20 @@ from .oracle import (  # noqa: F401
     gemm_s32,
     lib_path,
     num_threads,
+    pack_bits,
     pack_codes,
     pack_codes_fp6,
     pack_weights_fp4,
     unpack_codes_fp6,
     pack_weights,
     quantize_activations,
+    quantize_qkv,
     quantize_weights,
     round_bf16,
     set_num_threads,
     swiglu,
+    unpack_bits,
     unpack_codes,
+    dequantize_qkv,
     unpack_weights,
 )

@@ -303,6 +303,87 @@ void orc_round_bf16(const float* in, int64_t n, uint16_t* out) {
 }
 
 /* ------------------------------------------------------------------------------------
+ * QKV state quantisation [V2, text of Tables 2 and 3 (low-bit attention): the Q, K and V
+ * states are quantised after RoPE, each head directly to unsigned integers with the absmax
+ * function and no calibration data; a 3-bit KV cache keeps the accuracy of a full-precision
+ * one].  Reading: a head vector x of length d is mapped linearly from [-g, g], g = max|x|,
+ * onto the unsigned grid 0 .. L with L = 2^bits - 1 (both ends reachable):
+ *     s = fl32(L / fl32(2g)),   c = L/2 (exact),
+ *     u = clamp(rint_ne(fl32(fl32(x*s) + c)), 0, L)
+ * and g < 2^-120 takes s = 0, so a zero head gives u = rint_ne(c) everywhere.
+ * Reconstruction: xhat = fl32(fl32(u - c) * D) with D = fl32(fl32(2g) / L).
+ * u: rows*d unpacked codes (uint8); gamma: one g per head row.
+ * ------------------------------------------------------------------------------------ */
+int orc_quantize_qkv(const void* x, int dtype, int64_t rows, int64_t d, int bits, uint8_t* u, float* gamma) {
+  if (rows < 0 || d <= 0 || bits < 2 || bits > 8) return -1;
+  if (rows > 0 && (!x || !u || !gamma)) return -1;
+  const float L = (float)((1 << bits) - 1);
+  const float c = L / 2.0f;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    float g = 0.0f;
+    for (int64_t i = 0; i < d; ++i) {
+      float a = fabsf(load_x(x, dtype, r * d + i));
+      if (a > g) g = a;
+    }
+    gamma[r] = g;
+    const float s = g < 0x1p-120f ? 0.0f : L / (2.0f * g);
+    for (int64_t i = 0; i < d; ++i) {
+      float v = load_x(x, dtype, r * d + i) * s;
+      v = rintf(v + c);
+      if (v < 0.0f) v = 0.0f;
+      if (v > L) v = L;
+      u[r * d + i] = (uint8_t)v;
+    }
+  }
+  return 0;
+}
+
+int orc_dequantize_qkv(const uint8_t* u, const float* gamma, int64_t rows, int64_t d, int bits, float* out) {
+  if (rows < 0 || d <= 0 || bits < 2 || bits > 8) return -1;
+  const float L = (float)((1 << bits) - 1);
+  const float c = L / 2.0f;
+  for (int64_t r = 0; r < rows; ++r) {
+    const float D = (2.0f * gamma[r]) / L;
+    for (int64_t i = 0; i < d; ++i) out[r * d + i] = ((float)u[r * d + i] - c) * D;
+  }
+  return 0;
+}
+
+/* b-bit codes, least significant bit first: code i of a row occupies bits [b*i, b*i + b) of
+ * the row's little-endian bit string; rows of d*b/8 bytes (d*b % 8 == 0). */
+int orc_pack_bits(const uint8_t* u, int64_t rows, int64_t d, int bits, uint8_t* out) {
+  if (rows < 0 || d <= 0 || bits < 1 || bits > 8 || (d * bits) % 8 != 0) return -1;
+  const int64_t rb = d * bits / 8;
+  memset(out, 0, (size_t)(rows * rb));
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t i = 0; i < d; ++i) {
+      const unsigned v = u[r * d + i];
+      if (v >> bits) return -1;
+      for (int b = 0; b < bits; ++b) {
+        const int64_t bit = i * bits + b;
+        if ((v >> b) & 1u) out[r * rb + bit / 8] |= (uint8_t)(1u << (bit % 8));
+      }
+    }
+  return 0;
+}
+
+int orc_unpack_bits(const uint8_t* in, int64_t rows, int64_t d, int bits, uint8_t* u) {
+  if (rows < 0 || d <= 0 || bits < 1 || bits > 8 || (d * bits) % 8 != 0) return -1;
+  const int64_t rb = d * bits / 8;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t i = 0; i < d; ++i) {
+      unsigned v = 0;
+      for (int b = 0; b < bits; ++b) {
+        const int64_t bit = i * bits + b;
+        v |= (unsigned)((in[r * rb + bit / 8] >> (bit % 8)) & 1u) << b;
+      }
+      u[r * d + i] = (uint8_t)v;
+    }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------------------
  * Packed formats (the header of the C ABI documents them; not given by the pages).
  * ------------------------------------------------------------------------------------ */
 

@@ -68,6 +68,14 @@ def _load():
         lib.orc_forward.restype = I
         lib.orc_swiglu.argtypes = [P, P, I64, P]
         lib.orc_round_bf16.argtypes = [P, I64, P]
+        lib.orc_quantize_qkv.argtypes = [P, I, I64, I64, I, P, P]
+        lib.orc_quantize_qkv.restype = I
+        lib.orc_dequantize_qkv.argtypes = [P, P, I64, I64, I, P]
+        lib.orc_dequantize_qkv.restype = I
+        lib.orc_pack_bits.argtypes = [P, I64, I64, I, P]
+        lib.orc_pack_bits.restype = I
+        lib.orc_unpack_bits.argtypes = [P, I64, I64, I, P]
+        lib.orc_unpack_bits.restype = I
         lib.orc_pack_weights.argtypes = [P, I64, I64, P]
         lib.orc_pack_weights.restype = I
         lib.orc_unpack_weights.argtypes = [P, I64, I64, P]
@@ -229,6 +237,48 @@ def ffn_forward(x, Tg, ag: float, Tu, au: float, Td, ad: float, abits: int = 4, 
         h = round_bf16(h)
     y = forward(h, Td, ad, abits, True, norm=True, gamma=gamma_down, eps=eps)
     return (y, h) if intermediates else y
+
+
+def quantize_qkv(x, bits: int):
+    """Per-head unsigned absmax quantisation of post-RoPE Q/K/V head vectors.
+
+    x: [rows, d] float32 or bf16 patterns (one row per token and head).
+    Returns (u uint8 [rows, d] unpacked codes in 0 .. 2^bits - 1, gamma f32 [rows])."""
+    x = np.ascontiguousarray(x)
+    rows, d = x.shape
+    u = np.empty((rows, d), np.uint8)
+    g = np.empty(rows, np.float32)
+    if _load().orc_quantize_qkv(_p(x), _xdtype(x), rows, d, int(bits), _p(u), _p(g)) != 0:
+        raise ValueError("orc_quantize_qkv: bad arguments")
+    return u, g
+
+
+def dequantize_qkv(u, gamma, bits: int) -> np.ndarray:
+    u = _c(u, np.uint8)
+    gamma = _c(gamma, np.float32)
+    rows, d = u.shape
+    out = np.empty((rows, d), np.float32)
+    if _load().orc_dequantize_qkv(_p(u), _p(gamma), rows, d, int(bits), _p(out)) != 0:
+        raise ValueError("orc_dequantize_qkv: bad arguments")
+    return out
+
+
+def pack_bits(u, bits: int) -> np.ndarray:
+    u = _c(u, np.uint8)
+    rows, d = u.shape
+    out = np.empty((rows, d * bits // 8), np.uint8)
+    if _load().orc_pack_bits(_p(u), rows, d, int(bits), _p(out)) != 0:
+        raise ValueError("orc_pack_bits: bad arguments or code out of range")
+    return out
+
+
+def unpack_bits(packed, d: int, bits: int) -> np.ndarray:
+    packed = _c(packed, np.uint8)
+    rows = packed.shape[0]
+    u = np.empty((rows, d), np.uint8)
+    if _load().orc_unpack_bits(_p(packed), rows, d, int(bits), _p(u)) != 0:
+        raise ValueError("orc_unpack_bits: bad arguments")
+    return u
 
 
 def pack_weights(T) -> np.ndarray:
