@@ -112,6 +112,8 @@ def main():
         return bench_ffn(args, wl)
     if wl.name == "decode_7b":
         return bench_decode(args, wl)
+    if wl.name == "kv_7b":
+        return bench_kv(args, wl)
     abits = args.abits
     M, K, N = wl.M, wl.K, wl.N
     dev = torch.device("cuda:0")
@@ -437,6 +439,63 @@ def bench_decode(args, wl):
                         "frac": head["gemv_gbs"] / PEAK_HBM_GBS, "traffic": None,
                         "kernel": "k_gemv (decode GEMM, v_mfma_i32_16x16x64_i8)",
                         "algorithmic": "N*K/4 weight bytes + M*K/2 code bytes + 4*M*N output bytes per launch"}}
+    print(json.dumps(out), flush=True)
+
+
+def bench_kv(args, wl):
+    """Unsigned absmax quantisation of post-RoPE K (or V) states into a 3-bit KV cache:
+    8192 tokens x 32 heads x 128, bf16 in.  HBM-bound; reported against 8 TB/s.  A step is
+    one launch over all 262144 head rows."""
+    import numpy as np
+    import torch
+
+    from bit_quantized_gemm_bitlinear_amd import binding as B
+    from bit_quantized_gemm_bitlinear_amd import inputs
+
+    T, H, d, bits = wl.M, wl.extra["heads"], wl.extra["head_dim"], wl.extra["bits"]
+    rows = T * H
+    rng = np.random.default_rng(inputs.SEED_X)
+    x = rng.standard_normal((rows, d)) * np.exp(rng.uniform(-4, 4, (rows, 1)))
+    x[:, :3] *= 20.0
+    xd = torch.from_numpy(inputs.f32_to_bf16_bits(x.astype(np.float32)).view(np.int16)).cuda().view(torch.bfloat16)
+    del x
+    # five copies (335 MB) used in turn, so the input is read from HBM, not the 256 MB Infinity Cache
+    xs = [xd] + [xd.clone() for _ in range(4)]
+    L = B.lib()
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    codes = torch.empty((rows, d * bits // 8), dtype=torch.uint8, device="cuda")
+    gamma = torch.empty(rows, dtype=torch.float32, device="cuda")
+
+    def step(i):
+        if L.hbl_quantize_qkv(xs[i % len(xs)].data_ptr(), B.HBL_BF16, rows, d, bits, codes.data_ptr(),
+                              gamma.data_ptr(), sh):
+            raise RuntimeError(L.hbl_last_error().decode())
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    el = (time.perf_counter() - t0) / args.steps
+    t_k = e0.elapsed_time(e1) * 1e-3 / args.steps
+    nbytes = rows * d * 2 + rows * d * bits // 8 + 4 * rows
+    gbs = nbytes / t_k / 1e9
+    log(f"[bench] kv quant {t_k * 1e6:.2f} us per launch, {gbs:.0f} GB/s")
+    out = {"metric": "3-bit KV-cache quantisation tokens/s (unsigned absmax per head, 7B-like K states)",
+           "value": T / el, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": el * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "f32", "data": "synthetic",
+           "config": {"workload": f"{wl.name}: {wl.description}", "tokens": T, "heads": H, "head_dim": d,
+                      "bits": bits},
+           "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": gbs / PEAK_HBM_GBS, "traffic": None, "kernel": "k_qkv_quant<3, bf16, 4>",
+                        "algorithmic": f"{d * 2 + d * bits // 8 + 4} B per head row (read bf16, write codes + gamma)"}}
     print(json.dumps(out), flush=True)
 
 

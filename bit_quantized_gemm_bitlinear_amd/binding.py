@@ -62,6 +62,9 @@ def lib() -> ctypes.CDLL:
             "hbl_gate_up_swiglu": (I, [P, P, P, P, P, I64, I64, I64, I, I, P, P]),
             "hbl_ffn_workspace_bytes": (SZ, [I64, I64, I64, I, I]),
             "hbl_ffn_forward": (I, [P, I, P, P, P, P, P, I64, I64, I64, I, P, P, F, I, P, P, SZ, P]),
+            "hbl_packed_qkv_bytes": (SZ, [I64, I64, I]),
+            "hbl_quantize_qkv": (I, [P, I, I64, I64, I, P, P, P]),
+            "hbl_dequantize_qkv": (I, [P, P, I64, I64, I, P, P]),
             "hbl_status_string": (ctypes.c_char_p, [I]),
             "hbl_last_error": (ctypes.c_char_p, []),
             "hbl_version": (I, []),
@@ -253,6 +256,30 @@ def ffn_forward(x, Wgu, scale_gate, scale_up, Wq_down, scale_down, abits: int = 
                                  _ptr(scale_down), M, D, F, int(abits), _ptr(gamma_in), _ptr(gamma_down), float(eps),
                                  _hdtype(h_dtype), _ptr(y), _ptr(ws), ws.numel(), _stream()))
     return y
+
+
+# ---- QKV states -----------------------------------------------------------------------------
+
+def quantize_qkv(x, bits: int):
+    """x [rows, d] (post-RoPE head vectors, bf16/fp32) -> (codes uint8 [rows, d*bits/8], gamma fp32 [rows])."""
+    import torch
+
+    _dev(x)
+    rows, d = x.shape
+    codes = torch.empty((rows, d * bits // 8), dtype=torch.uint8, device=x.device)
+    gamma = torch.empty(rows, dtype=torch.float32, device=x.device)
+    _check(lib().hbl_quantize_qkv(_ptr(x), _xdtype(x), rows, d, int(bits), _ptr(codes), _ptr(gamma), _stream()))
+    return codes, gamma
+
+
+def dequantize_qkv(codes, gamma, d: int, bits: int):
+    import torch
+
+    _dev(codes, gamma)
+    rows = codes.shape[0]
+    out = torch.empty((rows, d), dtype=torch.float32, device=codes.device)
+    _check(lib().hbl_dequantize_qkv(_ptr(codes), _ptr(gamma), rows, d, int(bits), _ptr(out), _stream()))
+    return out
 
 
 # ---- FP6 x FP4 a4 path -------------------------------------------------------------------

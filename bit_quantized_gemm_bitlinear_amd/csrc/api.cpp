@@ -437,6 +437,58 @@ hbl_status hbl_ffn_forward(const void* x, hbl_dtype xt, const uint8_t* Wgu, cons
   }
 }
 
+namespace {
+hbl_status check_qkv(const char* fn, int64_t rows, int64_t d, int bits) {
+  if (rows < 0 || rows > INT32_MAX) return fail(HBL_ERR_INVALID_ARG, fn, "rows must be in [0, 2^31)");
+  if (bits < 2 || bits > 8) return fail(HBL_ERR_INVALID_ARG, fn, "bits must be in 2..8");
+  if (d != 32 && d != 64 && d != 128 && d != 256 && d != 512)
+    return fail(HBL_ERR_UNSUPPORTED, fn, "head size d must be 32, 64, 128, 256 or 512");
+  return HBL_OK;
+}
+}  // namespace
+
+size_t hbl_packed_qkv_bytes(int64_t rows, int64_t d, int bits) {
+  if (rows < 0 || rows > INT32_MAX || bits < 2 || bits > 8 ||
+      (d != 32 && d != 64 && d != 128 && d != 256 && d != 512))
+    return 0;
+  return (size_t)(rows * d * bits / 8);
+}
+
+hbl_status hbl_quantize_qkv(const void* x, hbl_dtype xt, int64_t rows, int64_t d, int bits, uint8_t* codes,
+                            float* gamma, void* stream) {
+  static const char* fn = "hbl_quantize_qkv";
+  try {
+    HBL_TRY(check_qkv(fn, rows, d, bits));
+    if (xt != HBL_F32 && xt != HBL_BF16) return fail(HBL_ERR_INVALID_ARG, fn, "unknown dtype");
+    if (rows == 0) return HBL_OK;
+    HBL_TRY(check_ptr(fn, x, "x", 16));
+    HBL_TRY(check_ptr(fn, codes, "codes", 16));
+    HBL_TRY(check_ptr(fn, gamma, "gamma", 4));
+    hipError_t e = hbl::launch_qkv_quant(x, (int)xt, rows, d, bits, codes, gamma, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return HBL_OK;
+  } catch (...) {
+    return fail(HBL_ERR_HIP, fn, "unexpected C++ exception");
+  }
+}
+
+hbl_status hbl_dequantize_qkv(const uint8_t* codes, const float* gamma, int64_t rows, int64_t d, int bits, float* out,
+                              void* stream) {
+  static const char* fn = "hbl_dequantize_qkv";
+  try {
+    HBL_TRY(check_qkv(fn, rows, d, bits));
+    if (rows == 0) return HBL_OK;
+    HBL_TRY(check_ptr(fn, codes, "codes", 16));
+    HBL_TRY(check_ptr(fn, gamma, "gamma", 4));
+    HBL_TRY(check_ptr(fn, out, "out", 16));
+    hipError_t e = hbl::launch_qkv_dequant(codes, gamma, rows, d, bits, out, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return HBL_OK;
+  } catch (...) {
+    return fail(HBL_ERR_HIP, fn, "unexpected C++ exception");
+  }
+}
+
 hbl_status hbl_swiglu(const float* g, const float* u, int64_t n, float* h, void* stream) {
   static const char* fn = "hbl_swiglu";
   try {

@@ -38,6 +38,13 @@ hipError_t launch_gemm_f6f4(const uint8_t* codes6, const float* deq, const uint8
 // 2-bit ternary words -> FP4 E2M1 nibbles (k_gemm_f6f4.hip).
 hipError_t launch_weights_fp4(const uint8_t* Wq, int64_t N, int64_t K, uint8_t* Wq4, hipStream_t s);
 
+// Unsigned absmax quantisation of head vectors and its inverse (k_qkv.hip); d in
+// {32, 64, 128, 256, 512}, bits in 2..8, xt 0 fp32 / 1 bf16.
+hipError_t launch_qkv_quant(const void* x, int xt, int64_t rows, int64_t d, int bits, uint8_t* codes, float* gamma,
+                            hipStream_t s);
+hipError_t launch_qkv_dequant(const uint8_t* codes, const float* gamma, int64_t rows, int64_t d, int bits, float* out,
+                              hipStream_t s);
+
 // h = silu(g) * u (k_swiglu.hip).
 hipError_t launch_swiglu(const float* g, const float* u, int64_t n, float* h, hipStream_t s);
 

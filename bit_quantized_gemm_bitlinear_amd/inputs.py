@@ -142,4 +142,9 @@ WORKLOADS = {
                     "K=16384, N=4096, the wdown_7b activation recipe, a fresh weight matrix per step "
                     "(48 copies rotated, 805 MB, so weights stream from HBM)",
         extra={"batches": (1, 4, 16, 64), "weight_copies": 48}),
+    "kv_7b": Workload(
+        "kv_7b", 8192, 128, 32, (3,), False, False, "normal", 0.0, 1.0,
+        description="7B-like K (or V) states after RoPE: 8192 tokens x 32 heads x 128, bf16 N(0,1) with a "
+                    "per-head scale exp(U(-4,4)) and 3 outlier dimensions x20; unsigned absmax, 3-bit KV cache",
+        extra={"heads": 32, "head_dim": 128, "bits": 3}),
 }

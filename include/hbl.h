@@ -237,6 +237,24 @@ hbl_status hbl_forward_fp6fp4(const void* x, hbl_dtype xt, const uint8_t* Wq4, c
                               int64_t K, int64_t N, int use_hadamard, hbl_norm norm, const float* gamma,
                               float norm_eps, float* y, void* ws, size_t ws_bytes, void* stream);
 
+/* ---- QKV states (low-bit attention) -----------------------------------------------------
+ * The BitNet v2 write-up (text of Tables 2 and 3) quantises the Q, K and V states after RoPE,
+ * each head directly to unsigned integers with the absmax function and no calibration data,
+ * and keeps the KV cache at 3 bits.  Reading implemented here, per head vector x of length d
+ * (one row per token and head, post-RoPE, supplied by the caller), L = 2^bits - 1:
+ *     g = max|x|,  s = fl32(L / fl32(2g)) (s = 0 if g < 2^-120),  c = L/2,
+ *     u = clamp(rint_ne(fl32(fl32(x*s) + c)), 0, L)
+ * so [-g, g] maps onto 0 .. L with both ends reachable.  Inverse:
+ *     xhat = fl32(fl32(u - c) * fl32(fl32(2g) / L)).
+ * codes — rows of d*bits/8 bytes; code i of a row at bits [bits*i, bits*i + bits) of the row
+ *     read as a little-endian bit string.  gamma — one fp32 g per row.
+ * Limits: d in {32, 64, 128, 256, 512}; 2 <= bits <= 8. */
+size_t hbl_packed_qkv_bytes(int64_t rows, int64_t d, int bits);   /* rows*d*bits/8 */
+hbl_status hbl_quantize_qkv(const void* x, hbl_dtype xt, int64_t rows, int64_t d, int bits, uint8_t* codes,
+                            float* gamma, void* stream);
+hbl_status hbl_dequantize_qkv(const uint8_t* codes, const float* gamma, int64_t rows, int64_t d, int bits, float* out,
+                              void* stream);
+
 /* Static text for a status code, and the detail of the last failure on this thread. */
 const char* hbl_status_string(hbl_status s);
 const char* hbl_last_error(void);

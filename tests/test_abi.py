@@ -228,3 +228,20 @@ def _ffn(L, x=FAKE, xt=B.HBL_BF16, M=16, D=256, F=512, abits=4, ht=B.HBL_BF16, y
 ])
 def test_ffn_forward_rejects(L, kw, status):
     assert _ffn(L, **kw) == status
+
+
+def test_qkv_rejects(L):
+    assert L.hbl_packed_qkv_bytes(10, 128, 3) == 10 * 48
+    assert L.hbl_packed_qkv_bytes(10, 96, 3) == 0
+    q = L.hbl_quantize_qkv
+    assert q(FAKE, 1, 10, 96, 3, FAKE, FAKE, S) == B.HBL_ERR_UNSUPPORTED
+    assert q(FAKE, 1, 10, 128, 9, FAKE, FAKE, S) == B.HBL_ERR_INVALID_ARG
+    assert q(FAKE, 1, 10, 128, 1, FAKE, FAKE, S) == B.HBL_ERR_INVALID_ARG
+    assert q(FAKE, 5, 10, 128, 3, FAKE, FAKE, S) == B.HBL_ERR_INVALID_ARG
+    assert q(FAKE, 1, -1, 128, 3, FAKE, FAKE, S) == B.HBL_ERR_INVALID_ARG
+    assert q(FAKE_MIS, 1, 10, 128, 3, FAKE, FAKE, S) == B.HBL_ERR_INVALID_ARG
+    assert q(FAKE, 1, 10, 128, 3, None, FAKE, S) == B.HBL_ERR_INVALID_ARG
+    assert q(None, 1, 0, 128, 3, None, None, S) == B.HBL_OK
+    dq = L.hbl_dequantize_qkv
+    assert dq(FAKE, FAKE, 10, 128, 3, FAKE_MIS, S) == B.HBL_ERR_INVALID_ARG
+    assert dq(FAKE, None, 10, 128, 3, FAKE, S) == B.HBL_ERR_INVALID_ARG
