@@ -32,6 +32,7 @@ if ROOT not in sys.path:
 METRIC = "H-BitLinear a4 tokens/s + effective TOPS (% int8 MFMA peak), 7B-like Wdown"
 PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, 5.0 POP/s
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
+PEAK_FP4_TFLOPS = 10100.0    # MI355X dense FP6 / FP4 MFMA, 10.1 PFLOP/s
 
 
 def log(*a):
@@ -47,6 +48,7 @@ def parse():
     p.add_argument("--abits", type=int, default=4)
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time of the CPU baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-alt", action="store_true", help="skip the FP6 x FP4 path measured beside the headline")
     p.add_argument("--copy-mb", type=int, default=0,
                    help="only run a plain device-to-device copy of this many MiB (3 times) and exit; used to "
                         "calibrate the FETCH_SIZE / WRITE_SIZE counters")
@@ -198,6 +200,56 @@ def main():
     log(f"[bench] act-quant {t_act * 1e6:.1f} us ({act_gbs:.0f} GB/s), gemm {t_gemm * 1e6:.1f} us "
         f"({gemm_tops:.0f} TOPS), effective {eff_tops:.0f} TOPS")
 
+    # ---- the same a4 forward on the FP6 x FP4 path (bit-identical outputs), reported beside ----
+    alt = None
+    if abits == 4 and not args.no_alt:
+        Wq4 = B.weights_to_fp4(Wq, K)
+        ws6 = torch.empty(max(L.hbl_forward_fp6fp4_workspace_bytes(M, K), 256), dtype=torch.uint8, device=dev)
+        y6 = torch.empty_like(y)
+        c6 = ws6[:M * K // 4 * 3]
+        d6 = ws6[(M * K // 4 * 3 + 255) // 256 * 256:][:4 * M].view(torch.float32)
+
+        def ok(st):
+            if st != 0:
+                raise RuntimeError(L.hbl_last_error().decode())
+
+        def step6():
+            ok(L.hbl_forward_fp6fp4(x.data_ptr(), xt, Wq4.data_ptr(), scale.data_ptr(), M, K, N, int(wl.use_hadamard),
+                                    norm, None, 1e-5, y6.data_ptr(), ws6.data_ptr(), ws6.numel(), sh))
+
+        for _ in range(args.warmup):
+            step6()
+        torch.cuda.synchronize()
+        t6 = time.perf_counter()
+        for _ in range(args.steps):
+            step6()
+        torch.cuda.synchronize()
+        el6 = time.perf_counter() - t6
+        ev6 = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_ev)]
+        for i in range(n_ev):
+            ev6[i][0].record(stream)
+            ok(L.hbl_quantize_activations_fp6(x.data_ptr(), xt, M, K, norm, None, 1e-5, int(wl.use_hadamard),
+                                              c6.data_ptr(), d6.data_ptr(), sh))
+            ev6[i][1].record(stream)
+            ok(L.hbl_gemm_fp6fp4_dequant(c6.data_ptr(), d6.data_ptr(), Wq4.data_ptr(), scale.data_ptr(), M, K, N,
+                                         y6.data_ptr(), sh))
+            ev6[i][2].record(stream)
+        torch.cuda.synchronize()
+        ta6 = sum(e[0].elapsed_time(e[1]) for e in ev6) / n_ev * 1e-3
+        tg6 = sum(e[1].elapsed_time(e[2]) for e in ev6) / n_ev * 1e-3
+        same = bool(torch.equal(y6.view(torch.int32), y.view(torch.int32)))
+        g6 = ops / tg6 / 1e12
+        alt = {"path": "FP6 (E2M3) INT4 codes x FP4 (E2M1) ternary weights, v_mfma_scale_f32_32x32x64_f8f6f4",
+               "dtype": "fp6xfp4", "value": M * args.steps / el6, "unit": "tokens/s",
+               "ms_per_step": el6 * 1e3 / args.steps, "outputs_bit_identical_to_int8_path": same,
+               "kernels_us": {"actquant_fwht_fp6": ta6 * 1e6, "gemm_fp6fp4_dequant": tg6 * 1e6},
+               "roofline": {"bound": "mfma", "achieved": g6, "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s",
+                            "frac": g6 / PEAK_FP4_TFLOPS, "traffic": None, "kernel": "k_gemm_f6f4<256, 256, 4, 2, 1>",
+                            "algorithmic": "2*M*N*K ops per launch"}}
+        log(f"[bench] fp6xfp4 path: {el6 * 1e3 / args.steps:.4f} ms/step, act {ta6 * 1e6:.1f} us, gemm "
+            f"{tg6 * 1e6:.1f} us ({g6:.0f} TFLOP/s), outputs identical: {same}")
+        del Wq4, ws6, y6
+
     gemm_kernel = f"k_gemm<{abits}, 256, 256, 2, 4, {256 if abits == 4 else 128}, 1>"
     act_kernel = f"k_actquant_h<{K.bit_length() - 1}, {abits}, 1, 1>"
 
@@ -254,6 +306,7 @@ def main():
                               "algorithmic": f"{act_bytes_per_token(K, abits, x_bytes)} B per token "
                                              "(read x, write packed codes + deq)"},
         "cpu_baseline": cpu,
+        "alt_fp6fp4": alt,
     }
     print(json.dumps(out), flush=True)
 

@@ -12,8 +12,12 @@
 // 32*(l/32) .. +31 of the 64-deep step; A as 6 registers of packed 6-bit codes, B as 4
 // registers of packed nibbles).
 //
-// Tiling follows the int8 kernel: 256 x 256 block tile, 8 waves of 128 x 64, K staged through
-// double-buffered LDS 128 deep, fragments read one k-step ahead.
+// Tiling: a 512-thread block computes a 256 x 256 tile with 4 x 2 waves of 64 x 128 (128 fp32
+// accumulators per lane, two waves per SIMD).  FP6/FP4 fragments are larger per MFMA than the
+// int8 path's packed INT4/2-bit fragments (40 bytes per lane per 64-deep step), so LDS and L2
+// traffic per MFMA is higher; the wave shape keeps A (the larger operand) read by only two
+// waves.  K is staged through double-buffered LDS 128 deep; see the main loop for the
+// software pipeline.
 #include "hbl_device.h"
 #include "hbl_internal.h"
 
@@ -55,7 +59,7 @@ __global__ __launch_bounds__(64 * WR * WC) void k_gemm_f6f4(const uint8_t* __res
   constexpr int ACH = AB / 16, BCH = BB / 16;
   constexpr int ALD = BM * ACH / NT, BLD = BN * BCH / NT;
   static_assert(ALD * NT == BM * ACH && BLD * NT == BN * BCH, "tile/thread mismatch");
-  static_assert(KS % 2 == 0, "even k-steps per stage");
+  static_assert(KS == 2, "the pipelined loop is written for two k-steps per stage");
 
   __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * AS];
   __shared__ __attribute__((aligned(16))) uint8_t sB[2][BN * BS];
@@ -92,12 +96,25 @@ __global__ __launch_bounds__(64 * WR * WC) void k_gemm_f6f4(const uint8_t* __res
     const int va = n64 * 48 / 16, vb = n64 * 32 / 16;
     const uint8_t* ak = Ablk + (int64_t)kt * AB;
     const uint8_t* bk = Bblk + (int64_t)kt * BB;
+    // Chunks past the end are loaded from the last valid chunk of their row (always in
+    // bounds) and cleared with a mask the compiler cannot see through, so the loads stay
+    // unconditional and the loop body stays one basic block.
 #pragma unroll
-    for (int i = 0; i < ALD; ++i)
-      ra[i] = (int)((tid + NT * i) % ACH) < va ? *reinterpret_cast<const uint4*>(ak + aoff[i]) : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < ALD; ++i) {
+      const int c = (tid + NT * i) % ACH, back = c < va ? 0 : 16 * (c - va + 1);
+      uint32_t keep = c < va ? ~0u : 0u;
+      asm volatile("" : "+v"(keep));
+      const uint4 v = *reinterpret_cast<const uint4*>(ak + aoff[i] - back);
+      ra[i] = make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
+    }
 #pragma unroll
-    for (int i = 0; i < BLD; ++i)
-      rb[i] = (int)((tid + NT * i) % BCH) < vb ? *reinterpret_cast<const uint4*>(bk + boff[i]) : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < BLD; ++i) {
+      const int c = (tid + NT * i) % BCH, back = c < vb ? 0 : 16 * (c - vb + 1);
+      uint32_t keep = c < vb ? ~0u : 0u;
+      asm volatile("" : "+v"(keep));
+      const uint4 v = *reinterpret_cast<const uint4*>(bk + boff[i] - back);
+      rb[i] = make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
+    }
   };
   auto swrite = [&](int buf) {
 #pragma unroll
@@ -152,6 +169,14 @@ __global__ __launch_bounds__(64 * WR * WC) void k_gemm_f6f4(const uint8_t* __res
     }
   };
 
+  // Software pipeline over two LDS buffers: the global loads of stage kt + 1 are issued at
+  // the start of stage kt and stored into the other buffer during its second k-step, and the
+  // fragments of each k-step are read during the MFMAs of the previous one.  The loop body
+  // has no branches (the last stage reloads itself into the idle buffer), so it is one
+  // scheduling region, and the group barriers interleave one memory instruction after each
+  // MFMA.  Two waves share each SIMD, so one wave's barrier or load wait is covered by the
+  // other's MFMAs.
+  constexpr int NMF = TM * TN;                 // MFMAs per k-step
   Frag f0, f1;
   gload(0, KT == 1 ? last_k64 : KS);
   swrite(0);
@@ -159,18 +184,25 @@ __global__ __launch_bounds__(64 * WR * WC) void k_gemm_f6f4(const uint8_t* __res
   fread(0, 0, f0);
   for (int kt = 0; kt < KT; ++kt) {
     const int buf = kt & 1;
-    const bool has_next = kt + 1 < KT;
-    if (has_next) gload(kt + 1, kt + 1 == KT - 1 ? last_k64 : KS);
+    const int nx = kt + 1 < KT ? kt + 1 : kt;
+    gload(nx, nx == KT - 1 ? last_k64 : KS);
+    fread(buf, 1, f1);
+    fmma(f0);
 #pragma unroll
-    for (int ks = 0; ks < KS; ks += 2) {
-      fread(buf, ks + 1, f1);
-      fmma(f0);
-      if (ks + 2 < KS) fread(buf, ks + 2, f0);
-      fmma(f1);
+    for (int i = 0; i < NMF; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      if (i < ALD + BLD) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one global load
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
     }
-    if (has_next) swrite(buf ^ 1);
+    swrite(buf ^ 1);
+    fmma(f1);
+#pragma unroll
+    for (int i = 0; i < NMF; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // one LDS write
+    }
     __syncthreads();
-    if (has_next) fread(buf ^ 1, 0, f0);
+    fread(buf ^ 1, 0, f0);
   }
 
   float alpha = 0.0f;
@@ -214,7 +246,7 @@ hipError_t launch(const uint8_t* codes, const float* deq, const uint8_t* Wq4, co
   const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
   const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
   if ((double)((t256 + CUS - 1) / CUS) * 2.0 <= (double)((t128 + CUS - 1) / CUS))
-    return launch_cfg<256, 256, 2, 4, MODE>(codes, deq, Wq4, w_scale, M, K, N, acc, y, s);
+    return launch_cfg<256, 256, 4, 2, MODE>(codes, deq, Wq4, w_scale, M, K, N, acc, y, s);
   return launch_cfg<128, 128, 2, 2, MODE>(codes, deq, Wq4, w_scale, M, K, N, acc, y, s);
 }
 
