@@ -72,11 +72,17 @@ __global__ __launch_bounds__(64 * GV_WAVES) void k_gemv(const uint8_t* __restric
   const int per = (ngroups + GV_WAVES - 1) / GV_WAVES;
   const int c0 = wave * per, c1 = min(ngroups, c0 + per);
 
-  // Rows past N (tokens past M) are clamped to the last one; their sums are never stored.
+  // Weight rows past N are clamped to the last one; their sums are never stored.  Token rows
+  // past M are not loaded at all (their codes are taken as zero), so a small M issues only the
+  // code loads it needs.
   const uint8_t* brow = B + (int64_t)min(n0 + r, N - 1) * (K / 4) + 16 * g;
   const uint8_t* arow[MT];
+  bool alive[MT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) arow[mt] = A + (int64_t)min(16 * mt + r, M - 1) * (K * ABITS / 8) + ACB * g;
+  for (int mt = 0; mt < MT; ++mt) {
+    alive[mt] = 16 * mt + r < M;
+    arow[mt] = A + (int64_t)min(16 * mt + r, M - 1) * (K * ABITS / 8) + ACB * g;
+  }
 
   v4i acc[MT];
 #pragma unroll
@@ -94,7 +100,7 @@ __global__ __launch_bounds__(64 * GV_WAVES) void k_gemv(const uint8_t* __restric
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int q = 0; q < ACB / 16; ++q)
-          ac[u][mt].v[q] = ok ? *reinterpret_cast<const uint4*>(arow[mt] + (int64_t)4 * ACB * (cb + u) + 16 * q)
+          ac[u][mt].v[q] = ok && alive[mt] ? *reinterpret_cast<const uint4*>(arow[mt] + (int64_t)4 * ACB * (cb + u) + 16 * q)
                               : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
