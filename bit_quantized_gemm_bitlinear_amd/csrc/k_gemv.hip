@@ -143,7 +143,7 @@ hipError_t launch_mode(const uint8_t* codes, const float* deq, const uint8_t* Wq
   const dim3 grid((unsigned)((N + 15) / 16)), block(64 * GV_WAVES);
   const int mt = (int)((M + 15) / 16);
   if (mt == 1)
-    hipLaunchKernelGGL((k_gemv<ABITS, 1, 8, MODE>), grid, block, 0, s, codes, deq, Wq, w_scale, (int)M, (int)N,
+    hipLaunchKernelGGL((k_gemv<ABITS, 1, 4, MODE>), grid, block, 0, s, codes, deq, Wq, w_scale, (int)M, (int)N,
                        (int)K, acc, y);
   else if (mt == 2)
     hipLaunchKernelGGL((k_gemv<ABITS, 2, 4, MODE>), grid, block, 0, s, codes, deq, Wq, w_scale, (int)M, (int)N,

@@ -101,3 +101,17 @@ def test_forward_fp6fp4_full_size_sampled_rows(orc):
     y_o = orc.forward(np.ascontiguousarray(x[rows]), T, alpha, 4, True, norm=True)
     assert rel_fro(y[rows], y_o) <= 1e-3
     assert_close_ulps(y[rows], y_o, 4, "wdown_7b fp6fp4")
+
+
+@pytest.mark.parametrize("M", [16, 300])
+def test_gemm_fp6fp4_max_k(orc, M):
+    """K = HBL_MAX_K (131072) at the extreme INT4 codes: fp32 partial sums stay exact integers."""
+    K, N = 131072, 40
+    note("fp6fp4 max K", M)
+    q = np.full((M, K), -7, np.int8)
+    q[1::3, ::5] = 7
+    T = np.ones((N, K), np.int8)
+    T[1::2] = -1
+    T[::3, ::7] = 0
+    acc = to_host(B.gemm_fp6fp4_s32(to_dev(orc.pack_codes_fp6(q)), to_dev(orc.pack_weights_fp4(T)), K))
+    np.testing.assert_array_equal(acc, orc.gemm_s32(q, T))

@@ -164,3 +164,20 @@ def test_swiglu(orc):
     u = rng.standard_normal(n).astype(np.float32)
     h = to_host(B.swiglu(to_dev(g), to_dev(u)))
     assert_close_ulps(h, orc.swiglu(g, u), 4, "swiglu")
+
+
+@pytest.mark.parametrize("M", [16, 65])
+@pytest.mark.parametrize("abits", [4, 8])
+def test_gemm_s32_max_k(orc, M, abits):
+    """K = HBL_MAX_K (131072) at the extreme codes: |acc| = 128 * K (int8) fits the int32
+    accumulator of both the decode (M = 16) and the tiled (M = 65) kernels exactly."""
+    K, N = 131072, 40
+    note("gemm max K", M, abits)
+    qv = -8 if abits == 4 else -128
+    q = np.full((M, K), qv, np.int8)
+    q[1::3, ::5] = 7 if abits == 4 else 127
+    T = np.ones((N, K), np.int8)
+    T[1::2] = -1
+    T[::3, ::7] = 0
+    acc = to_host(B.gemm_s32(to_dev(orc.pack_codes(q, abits)), to_dev(orc.pack_weights(T)), K, abits))
+    np.testing.assert_array_equal(acc, orc.gemm_s32(q, T))
