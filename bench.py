@@ -477,10 +477,13 @@ def bench_decode(args, wl):
         t_act = sum(e[0].elapsed_time(e[1]) for e in ev) / steps * 1e-3
         t_gemv = sum(e[1].elapsed_time(e[2]) for e in ev) / steps * 1e-3
         gemv_bytes = N * K // 4 + M * K // 2 + 4 * M + 4 + 4 * M * N
-        per[M] = {"us_per_step": el * 1e6, "tokens_per_s": M / el, "actquant_us": t_act * 1e6,
-                  "gemv_us": t_gemv * 1e6, "gemv_bytes": gemv_bytes, "gemv_gbs": gemv_bytes / t_gemv / 1e9}
-        log(f"[bench] decode M={M}: {el * 1e6:.2f} us/step, act {t_act * 1e6:.2f} us, gemv {t_gemv * 1e6:.2f} us "
-            f"({gemv_bytes / t_gemv / 1e9:.0f} GB/s)")
+        fused = bool(L.hbl_forward_fused(M, K, 4, 1))
+        per[M] = {"us_per_step": el * 1e6, "tokens_per_s": M / el,
+                  "path": "one fused kernel" if fused else "activation kernel + decode GEMM",
+                  "separate_calls_us": {"actquant": t_act * 1e6, "gemv": t_gemv * 1e6},
+                  "gemv_bytes": gemv_bytes, "gemv_gbs": gemv_bytes / t_gemv / 1e9}
+        log(f"[bench] decode M={M}: {el * 1e6:.2f} us/step ({per[M]['path']}); separate calls: act "
+            f"{t_act * 1e6:.2f} us, gemv {t_gemv * 1e6:.2f} us ({gemv_bytes / t_gemv / 1e9:.0f} GB/s)")
     head = per[wl.M]
     out = {"metric": "H-BitLinear a4 decode tokens/s, 7B-like Wdown (weights streamed from HBM)",
            "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": args.warmup,

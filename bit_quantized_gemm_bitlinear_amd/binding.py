@@ -49,6 +49,7 @@ def lib() -> ctypes.CDLL:
             "hbl_gemm_dequant": (I, [P, P, P, P, I64, I64, I64, I, P, P]),
             "hbl_forward": (I, [P, I, P, P, I64, I64, I64, I, I, I, P, F, P, P, SZ, P]),
             "hbl_swiglu": (I, [P, P, I64, P, P]),
+            "hbl_forward_fused": (I, [I64, I64, I, I]),
             "hbl_packed_weight_fp4_bytes": (SZ, [I64, I64]),
             "hbl_packed_act_fp6_bytes": (SZ, [I64, I64]),
             "hbl_forward_fp6fp4_workspace_bytes": (SZ, [I64, I64]),

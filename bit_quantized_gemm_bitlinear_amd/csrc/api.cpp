@@ -200,6 +200,12 @@ hbl_status hbl_forward(const void* x, hbl_dtype xt, const uint8_t* Wq, const flo
     uint8_t* codes = static_cast<uint8_t*>(ws);
     float* deq = reinterpret_cast<float*>(codes + round256((size_t)(M * K * abits / 8)));
     hipStream_t s = (hipStream_t)stream;
+    if (hbl::decode_fused_ok(M, K, abits, use_hadamard)) {  // a few rows: one fused kernel
+      hipError_t e = hbl::launch_decode_fused(x, (int)xt, M, K, (int)norm, norm == HBL_NORM_RMS ? gamma : nullptr,
+                                              norm_eps, abits, Wq, w_scale, N, codes, deq, y, s);
+      if (e != hipSuccess) return hip_fail(fn, e);
+      return HBL_OK;
+    }
     hipError_t e = hbl::launch_actquant(x, (int)xt, M, K, (int)norm, norm == HBL_NORM_RMS ? gamma : nullptr,
                                         norm_eps, abits, use_hadamard, codes, deq, s);
     if (e != hipSuccess) return hip_fail(fn, e);
@@ -487,6 +493,12 @@ hbl_status hbl_dequantize_qkv(const uint8_t* codes, const float* gamma, int64_t 
   } catch (...) {
     return fail(HBL_ERR_HIP, fn, "unexpected C++ exception");
   }
+}
+
+int hbl_forward_fused(int64_t M, int64_t K, int abits, int use_hadamard) {
+  if (M < 1 || K < 64 || K % 64 != 0 || K > HBL_MAX_K || (use_hadamard != 0 && use_hadamard != 1)) return 0;
+  if (use_hadamard && !pow2(K)) return 0;
+  return hbl::decode_fused_ok(M, K, abits, use_hadamard) ? 1 : 0;
 }
 
 hbl_status hbl_swiglu(const float* g, const float* u, int64_t n, float* h, void* stream) {

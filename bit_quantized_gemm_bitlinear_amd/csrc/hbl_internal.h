@@ -16,6 +16,14 @@ hipError_t launch_wquant(const float* W, int64_t N, int64_t K, uint8_t* Wq, floa
 hipError_t launch_actquant(const void* x, int xt, int64_t M, int64_t K, int norm, const float* gamma,
                            float eps, int abits, int use_h, uint8_t* codes, float* deq, hipStream_t s);
 
+// The whole H-BitLinear forward for a few token rows in one kernel (k_actquant.hip): applies
+// when decode_fused_ok(M, K, abits, use_h); writes codes/deq (workspace) and y like the
+// two-kernel path, bit for bit.
+bool decode_fused_ok(int64_t M, int64_t K, int abits, int use_h);
+hipError_t launch_decode_fused(const void* x, int xt, int64_t M, int64_t K, int norm, const float* gamma, float eps,
+                               int abits, const uint8_t* Wq, const float* w_scale, int64_t N, uint8_t* codes,
+                               float* deq, float* y, hipStream_t s);
+
 // Integer GEMM with either an int32 output (acc != nullptr) or the dequantising epilogue
 // (y != nullptr) (k_gemm.hip).
 hipError_t launch_gemm(const uint8_t* codes, const float* deq, const uint8_t* Wq, const float* w_scale,

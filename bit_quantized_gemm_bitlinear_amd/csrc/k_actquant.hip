@@ -385,6 +385,214 @@ __global__ __launch_bounds__(block_threads<L>()) void k_actquant_h(
   }
 }
 
+// Decode-regime H-BitLinear forward in one kernel (M <= R token rows, R = rows the block
+// transforms at once: 1 for K = 16384, 2 for 8192, 4 for 4096).
+// With a handful of rows, the two-kernel path pays the latency of a one-block activation
+// kernel and then of the weight stream.  Here every block owns 16 output columns: it first
+// issues the loads of its whole weight slice (16 rows x K/4 bytes, kept in registers), then
+// transforms and quantises the M activation rows itself (the same code and the same fp32
+// operations as k_actquant_h, so codes and deq are bit-identical), leaving the codes as
+// int8 in LDS, and finally multiplies them with the weights on v_mfma_i32_16x16x64_i8.
+// Every block repeats the (cheap) activation work; block 0 also writes the packed codes and
+// deq to the caller's workspace, as the two-kernel path does.  The int32 sums are exact, so
+// y equals the two-kernel path bit for bit.
+constexpr int DEC_MAX_GROUPS = 1;  // one group of R rows: more rows are faster on the two-kernel path
+
+__device__ __forceinline__ v4i dec_b_operand(uint32_t w) {
+  return v4i{(int)((w << 6) & 0xC0C0C0C0u), (int)((w << 4) & 0xC0C0C0C0u), (int)((w << 2) & 0xC0C0C0C0u),
+             (int)(w & 0xC0C0C0C0u)};
+}
+
+template <int L, int ABITS, int XT, int NM>
+__global__ __launch_bounds__(block_threads<L>()) void k_decode_h(
+    const void* __restrict__ x, int M, const float* __restrict__ gamma, float eps, float hK,
+    const uint8_t* __restrict__ Wq, const float* __restrict__ w_scale, int N, uint8_t* __restrict__ codes,
+    float* __restrict__ deq, float* __restrict__ y) {
+  constexpr int K = 1 << L;
+  constexpr int T = K / 64;           // threads per row
+  constexpr int WG = block_threads<L>();
+  constexpr int R = WG / T;           // rows transformed at once
+  constexpr int NP = nphases(L);
+  constexpr int ROWF = K + K / 16;
+  constexpr int NW = WG / 64;
+  constexpr int MMAX = DEC_MAX_GROUPS * R;
+  constexpr int CST = K + 16;         // LDS stride of one row of int8 codes
+  constexpr int G = K / (NW * 256);   // 256-deep weight groups per wave
+  constexpr float Qb = QB<ABITS>::value;
+  static_assert(NP == 3 && G >= 1, "the fused decode kernel covers K = 2^12 .. 2^15");
+  __shared__ float lds[R * ROWF];
+  __shared__ __attribute__((aligned(16))) int8_t cl[MMAX * CST];
+  __shared__ float dl[MMAX];
+  __shared__ float redf[NW];
+  __shared__ double redd[NW];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rl = tid / T, t = tid % T;
+  const int gq = lane >> 4, rq = lane & 15;   // MFMA lane coordinates
+  const int n0 = blockIdx.x * 16;
+
+  // 1) The first activation rows, then the block's weights (lane (gq, rq) of wave w holds
+  //    chunk 4 (w G + u) + gq of row n0 + rq).  Loads complete in issue order, so the rows
+  //    go first: the transform can start while the weights are still streaming in.
+  RowChunk<XT> cur;
+  load_chunk<XT>(cur, x, (int64_t)min(rl, M - 1) * K + 64 * t);
+  __builtin_amdgcn_sched_barrier(0);  // keep the issue order
+  const uint8_t* brow = Wq + (int64_t)min(n0 + rq, N - 1) * (K / 4) + 16 * gq;
+  uint4 wb[G];
+#pragma unroll
+  for (int u = 0; u < G; ++u) wb[u] = *reinterpret_cast<const uint4*>(brow + 64 * (wave * G + u));
+
+  // 2) Activation rows, R at a time, exactly as k_actquant_h.
+  float g[64];
+  if constexpr (NM == 2) {
+    const float4* gp = reinterpret_cast<const float4*>(gamma + 64 * t);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float4 q = gp[i];
+      g[4 * i + 0] = q.x;
+      g[4 * i + 1] = q.y;
+      g[4 * i + 2] = q.z;
+      g[4 * i + 3] = q.w;
+    }
+  }
+  float* rowlds = lds + rl * ROWF;
+  auto process_group = [&](int grp) {
+    const int row = grp * R + rl;
+    const bool valid = row < M;
+    float v[64];
+    unpack_chunk<XT>(cur, v);
+    float r = 1.0f;
+    if constexpr (NM != 0) {
+      double ss = 0.0;
+#pragma unroll
+      for (int j = 0; j < 64; ++j) ss = __builtin_fma((double)v[j], (double)v[j], ss);
+      ss = row_sum<T>(ss, redd);
+      r = (float)(1.0 / sqrt(ss / (double)K + (double)eps));
+      if constexpr (NM == 2) {
+#pragma unroll
+        for (int j = 0; j < 64; ++j) v[j] *= g[j];
+      }
+    }
+    stages<0, phase_desc(L, 0).a>(v);
+    lds_write<L, 0, ROWF>(v, rowlds, t);
+    __syncthreads();
+    lds_read<L, 1, ROWF>(v, rowlds, t);
+    stages<Layout<L, 1>::c, Layout<L, 1>::a>(v);
+    lds_write<L, 1, ROWF>(v, rowlds, t);
+    __syncthreads();
+    lds_read<L, 2, ROWF>(v, rowlds, t);
+    stages<Layout<L, 2>::c, Layout<L, 2>::a>(v);
+
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 64; ++j) amax = fmaxf(amax, fabsf(v[j]));
+    amax = row_max<T>(amax, redf);
+    const bool zero = amax < 0x1p-120f;
+    const float s = zero ? 0.0f : Qb / amax;
+    using LY = Layout<L, 2>;
+    constexpr int RL = 1 << LY::c;     // runs of consecutive elements in registers
+    const int b = LY::base(t);
+    if (valid) {
+      // int8 codes (the low byte of the magic-number rounding, as in the INT8 packer)
+      int8_t* crow = cl + row * CST;
+#pragma unroll
+      for (int gi = 0; gi < 64 / RL; ++gi) {
+#pragma unroll
+        for (int d = 0; d < RL / 4; ++d) {
+          const float* q = v + gi * RL + 4 * d;
+          const uint32_t q0 = rne_bits(q[0] * s, 12582912.0f), q1 = rne_bits(q[1] * s, 12582912.0f);
+          const uint32_t q2 = rne_bits(q[2] * s, 12582912.0f), q3 = rne_bits(q[3] * s, 12582912.0f);
+          const uint32_t lo = __builtin_amdgcn_perm(q1, q0, 0x0c0c0400u);
+          const uint32_t hi = __builtin_amdgcn_perm(q3, q2, 0x04000c0cu);
+          *reinterpret_cast<uint32_t*>(crow + b + LY::off(gi * RL) + 4 * d) = lo | hi;
+        }
+      }
+      const float dq = zero ? 0.0f : __fmul_rn(__fmul_rn(amax / Qb, r), hK);
+      if (t == 0) dl[row] = dq;
+      if (blockIdx.x == 0) {
+        uint8_t* grow = codes + (int64_t)row * row_bytes<ABITS>(K);
+#pragma unroll
+        for (int gi = 0; gi < 64 / RL; ++gi) store_run<ABITS, RL>(v + gi * RL, s, grow, b + LY::off(gi * RL));
+        if (t == 0) deq[row] = dq;
+      }
+    }
+    __syncthreads();  // LDS and reduction slots are reused by the next group
+    };
+  // Group 0 is peeled out of the loop so that the wait for its input, issued before the
+  // weights, does not also wait for the weights.
+  process_group(0);
+  const int ngroups = (M + R - 1) / R;
+  for (int grp = 1; grp < ngroups; ++grp) {
+    load_chunk<XT>(cur, x, (int64_t)min(grp * R + rl, M - 1) * K + 64 * t);
+    process_group(grp);
+  }
+
+  // 3) The product: wave w covers groups [w G, w G + G) of K; step t of group C pairs k-block
+  //    4 (4C + gq) + t of the codes with word t of the weight chunk 4C + gq.
+  v4i acc4[4] = {v4i{0, 0, 0, 0}, v4i{0, 0, 0, 0}, v4i{0, 0, 0, 0}, v4i{0, 0, 0, 0}};  // independent chains
+  const bool arow_ok = rq < M;
+  const int8_t* arow = cl + rq * CST;
+#pragma unroll
+  for (int u = 0; u < G; ++u) {
+    const int C = wave * G + u;
+    const uint32_t w4[4] = {wb[u].x, wb[u].y, wb[u].z, wb[u].w};
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      v4i a = v4i{0, 0, 0, 0};
+      if (arow_ok) {
+        const uint4 av = *reinterpret_cast<const uint4*>(arow + 16 * (4 * (4 * C + gq) + tt));
+        a = v4i{(int)av.x, (int)av.y, (int)av.z, (int)av.w};
+      }
+      acc4[tt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, dec_b_operand(w4[tt]), acc4[tt], 0, 0, 0);
+    }
+  }
+  const v4i acc = acc4[0] + acc4[1] + acc4[2] + acc4[3];  // exact int32 sums
+
+  // 4) Sum the waves' tiles (lane l, register v: token 4 (l / 16) + v, column l % 16) and
+  //    dequantise: codes are int8 q and weights 64 t, so the sum is 64 times the product.
+  int* red = reinterpret_cast<int*>(lds);
+#pragma unroll
+  for (int vv = 0; vv < 4; ++vv) red[(wave * 4 + vv) * 64 + lane] = acc[vv];
+  __syncthreads();
+  if (tid < 4 * 64) {
+    const int vv = tid >> 6, l = tid & 63;
+    int sum = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) sum += red[(w * 4 + vv) * 64 + l];
+    const int m = 4 * (l >> 4) + vv, n = n0 + (l & 15);
+    if (m < M && n < N) y[(int64_t)m * N + n] = __fmul_rn(__fmul_rn((float)(sum >> 6), dl[m]), w_scale[0]);
+  }
+}
+
+template <int L, int ABITS, int XT>
+hipError_t launch_decode_l(const void* x, int64_t M, const float* gamma, float eps, int norm, const uint8_t* Wq,
+                           const float* w_scale, int64_t N, uint8_t* codes, float* deq, float* y, hipStream_t s) {
+  const float hK = (float)(1.0 / std::sqrt((double)(1 << L)));
+  const dim3 grid((unsigned)((N + 15) / 16)), block(block_threads<L>());
+  if (!norm)
+    hipLaunchKernelGGL((k_decode_h<L, ABITS, XT, 0>), grid, block, 0, s, x, (int)M, gamma, eps, hK, Wq, w_scale,
+                       (int)N, codes, deq, y);
+  else if (gamma == nullptr)
+    hipLaunchKernelGGL((k_decode_h<L, ABITS, XT, 1>), grid, block, 0, s, x, (int)M, gamma, eps, hK, Wq, w_scale,
+                       (int)N, codes, deq, y);
+  else
+    hipLaunchKernelGGL((k_decode_h<L, ABITS, XT, 2>), grid, block, 0, s, x, (int)M, gamma, eps, hK, Wq, w_scale,
+                       (int)N, codes, deq, y);
+  return hipGetLastError();
+}
+
+template <int ABITS, int XT>
+hipError_t dispatch_decode(int L, const void* x, int64_t M, const float* gamma, float eps, int norm,
+                           const uint8_t* Wq, const float* w_scale, int64_t N, uint8_t* codes, float* deq, float* y,
+                           hipStream_t s) {
+  switch (L) {
+    case 12: return launch_decode_l<12, ABITS, XT>(x, M, gamma, eps, norm, Wq, w_scale, N, codes, deq, y, s);
+    case 13: return launch_decode_l<13, ABITS, XT>(x, M, gamma, eps, norm, Wq, w_scale, N, codes, deq, y, s);
+    case 14: return launch_decode_l<14, ABITS, XT>(x, M, gamma, eps, norm, Wq, w_scale, N, codes, deq, y, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 // BitLinear path (no transform), any K with K % 64 == 0: one 256-thread block per row,
 // the row held in registers as NCH chunks of 8 consecutive elements per thread
 // (K <= 2048 * NCH), or streamed twice from memory when NCH == 0.
@@ -545,6 +753,28 @@ hipError_t dispatch_plain(const void* x, int64_t M, int64_t K, const float* gamm
 }
 
 }  // namespace
+
+bool decode_fused_ok(int64_t M, int64_t K, int abits, int use_h) {
+  if (!use_h || (abits != 4 && abits != 8) || M < 1) return false;
+  int L = 0;
+  while ((int64_t(1) << L) < K) ++L;
+  if (L < 12 || L > 14) return false;
+  const int64_t R = (int64_t)256 / ((int64_t(1) << L) / 64);  // rows per group (block of 256 threads)
+  return M <= DEC_MAX_GROUPS * R;
+}
+
+hipError_t launch_decode_fused(const void* x, int xt, int64_t M, int64_t K, int norm, const float* gamma, float eps,
+                               int abits, const uint8_t* Wq, const float* w_scale, int64_t N, uint8_t* codes,
+                               float* deq, float* y, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  int L = 0;
+  while ((int64_t(1) << L) < K) ++L;
+  if (abits == 4)
+    return xt ? dispatch_decode<4, 1>(L, x, M, gamma, eps, norm, Wq, w_scale, N, codes, deq, y, s)
+              : dispatch_decode<4, 0>(L, x, M, gamma, eps, norm, Wq, w_scale, N, codes, deq, y, s);
+  return xt ? dispatch_decode<8, 1>(L, x, M, gamma, eps, norm, Wq, w_scale, N, codes, deq, y, s)
+            : dispatch_decode<8, 0>(L, x, M, gamma, eps, norm, Wq, w_scale, N, codes, deq, y, s);
+}
 
 hipError_t launch_actquant(const void* x, int xt, int64_t M, int64_t K, int norm, const float* gamma, float eps,
                            int abits, int use_h, uint8_t* codes, float* deq, hipStream_t s) {

@@ -168,6 +168,12 @@ hbl_status hbl_forward(const void* x, hbl_dtype xt, const uint8_t* Wq, const flo
                        const float* gamma, float norm_eps, float* y, void* ws, size_t ws_bytes,
                        void* stream);
 
+/* 1 if hbl_forward(M, K, ..., abits, use_hadamard) runs as one fused kernel, else 0.  With a
+ * few token rows (use_hadamard, K = 4096 .. 16384, M <= 256 / (K / 64)), each block of the
+ * decode GEMM transforms and quantises the rows itself while its weights stream in; results
+ * (y, and the codes and deq left in the workspace) are identical to the two-kernel path. */
+int hbl_forward_fused(int64_t M, int64_t K, int abits, int use_hadamard);
+
 /* hbl_swiglu — the FFN gate of the LLaMA-like block (write-up section
  * "BitNet v2：原生4位激活": RMSNorm, SwishGLU, no bias):
  *  h[i] = fl32( silu(g[i]) * u[i] ),  silu(v) = v / (1 + exp(-v)) in fp32.

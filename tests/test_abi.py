@@ -245,3 +245,16 @@ def test_qkv_rejects(L):
     dq = L.hbl_dequantize_qkv
     assert dq(FAKE, FAKE, 10, 128, 3, FAKE_MIS, S) == B.HBL_ERR_INVALID_ARG
     assert dq(FAKE, None, 10, 128, 3, FAKE, S) == B.HBL_ERR_INVALID_ARG
+
+
+def test_forward_fused_query(L):
+    # one fused kernel only with the transform, K in 4096..16384 and M <= 256 / (K / 64)
+    assert L.hbl_forward_fused(1, 16384, 4, 1) == 1
+    assert L.hbl_forward_fused(2, 16384, 4, 1) == 0
+    assert L.hbl_forward_fused(2, 8192, 8, 1) == 1
+    assert L.hbl_forward_fused(4, 4096, 4, 1) == 1
+    assert L.hbl_forward_fused(5, 4096, 4, 1) == 0
+    assert L.hbl_forward_fused(1, 2048, 4, 1) == 0
+    assert L.hbl_forward_fused(1, 16384, 4, 0) == 0
+    assert L.hbl_forward_fused(0, 16384, 4, 1) == 0
+    assert L.hbl_forward_fused(1, 12288, 4, 1) == 0

@@ -92,3 +92,39 @@ def test_decode_forward_7b_wdown(orc, M):
     np.testing.assert_array_equal(codes, orc.pack_codes(q_o, 4))
     assert rel_fro(y, y_o) <= 1e-3
     assert_close_ulps(y, y_o, 4, "decode forward")
+
+
+# (K, M) inside the fused decode kernel's range (K = 2^12 .. 2^14, M up to the rows one
+# block transforms at once) and just outside it (two-kernel path; the comparison holds too)
+FUSED = [(16384, 1), (16384, 2), (8192, 1), (8192, 2), (8192, 3), (4096, 1), (4096, 3), (4096, 4), (4096, 5)]
+
+
+@pytest.mark.parametrize("K,M", FUSED)
+@pytest.mark.parametrize("variant", ["a4-bf16-rms", "a8-bf16-rms", "a4-fp32-none", "a4-bf16-gamma"])
+def test_fused_decode_equals_two_kernel_path(orc, K, M, variant):
+    """hbl_forward with a few rows runs one fused kernel; it must equal the separate
+    hbl_quantize_activations + hbl_gemm_dequant calls bit for bit (codes, deq and y)."""
+    torch = torch_mod()
+    abits = 8 if variant.startswith("a8") else 4
+    norm = not variant.endswith("none")
+    note("fused decode", K, M, variant)
+    x = inputs.make_activations("mixture", M, K, seed=K + M, outlier_frac=0.01, outlier_scale=50.0)
+    if "fp32" in variant:
+        x = inputs.bf16_bits_to_f32(x) * np.float32(3.0)
+    gamma = to_dev(np.random.default_rng(K).uniform(0.5, 1.5, K).astype(np.float32)) if "gamma" in variant else None
+    N = 300
+    Wq, scale = B.quantize_weights(to_dev(inputs.make_weights(N, K, seed=M)))
+    xd = to_dev(x)
+    ws = B.forward_workspace(M, K, abits)
+    y = B.forward(xd, Wq, scale, abits, True, norm=norm, gamma=gamma, ws=ws)
+    codes, deq = B.quantize_activations(xd, abits, True, norm=norm, gamma=gamma)
+    y2 = B.gemm_dequant(codes, deq, Wq, scale, K, abits)
+    torch.cuda.synchronize()
+    nb = M * K * abits // 8
+    assert torch.equal(ws[:nb], codes.view(-1))
+    assert torch.equal(ws[(nb + 255) // 256 * 256:][:4 * M].view(torch.float32).view(torch.int32), deq.view(torch.int32))
+    assert torch.equal(y.view(torch.int32), y2.view(torch.int32))
+    # and the oracle
+    T, alpha = orc.quantize_weights(inputs.make_weights(N, K, seed=M))
+    y_o = orc.forward(x, T, alpha, abits, True, norm=norm, gamma=None if gamma is None else to_host(gamma))
+    assert rel_fro(to_host(y), y_o) <= 1e-3
