@@ -152,10 +152,10 @@ int orc_quantize_weights(const float* W, int64_t N, int64_t K, int8_t* T, float*
  * quantiser, and the codes do not depend on how the RMS sum is ordered.
  * q: M*K int8 (unpacked), deq: M floats, rnorm (may be NULL): M floats of r.
  * ------------------------------------------------------------------------------------ */
-int orc_quantize_activations(const void* x, int dtype, int64_t M, int64_t K, int norm,
-                             const float* gamma, float eps, int abits, int use_h, int8_t* q, float* deq,
-                             float* rnorm) {
-  if (M < 0 || K <= 0 || (abits != 4 && abits != 8)) return -1;
+int orc_quantize_activations_stat(const void* x, int dtype, int64_t M, int64_t K, int norm,
+                                  const float* gamma, float eps, int abits, int use_h, int stat, int8_t* q,
+                                  float* deq, float* rnorm) {
+  if (M < 0 || K <= 0 || (abits != 4 && abits != 8) || (stat != 0 && stat != 1)) return -1;
   if (M > 0 && (!x || !q || !deq)) return -1;
   if (use_h && (K & (K - 1)) != 0) return -1;
   const int Qb = (abits == 4) ? 7 : 127;
@@ -182,6 +182,32 @@ int orc_quantize_activations(const void* x, int dtype, int64_t M, int64_t K, int
     if (norm) r = (float)(1.0 / sqrt(ss / (double)K + (double)eps));
     if (rnorm) rnorm[m] = r;
     if (use_h) orc_fwht_f32(z, K);
+    if (stat == 1) {
+      /* absmean statistic: the pages' absmean function (scale by the mean absolute value,
+       * round to the nearest integer, clip to the code range) applied to the INT4/INT8 grid:
+       * b = (float)(sum_k |z_k| in fp64, ascending / K); s = fl32(1 / b);
+       * q = clamp(rint_ne(fl32(z * s)), -Qb-1, Qb); deq = fl32(fl32(b * r) * hK). */
+      double sa = 0.0;
+      for (int64_t k = 0; k < K; ++k) sa += (double)fabsf(z[k]);
+      const float b = (float)(sa / (double)K);
+      if (b < 0x1p-120f) {
+        for (int64_t k = 0; k < K; ++k) q[m * K + k] = 0;
+        deq[m] = 0.0f;
+      } else {
+        const float s = 1.0f / b;
+        for (int64_t k = 0; k < K; ++k) {
+          float v = rintf(z[k] * s);
+          if (v > (float)Qb) v = (float)Qb;
+          if (v < (float)(-Qb - 1)) v = (float)(-Qb - 1);
+          q[m * K + k] = (int8_t)v;
+        }
+        float d = b * r;
+        d = d * hK;
+        deq[m] = d;
+      }
+      free(z);
+      continue;
+    }
     float g = 0.0f;
     for (int64_t k = 0; k < K; ++k) {
       float a = fabsf(z[k]);
@@ -206,6 +232,12 @@ int orc_quantize_activations(const void* x, int dtype, int64_t M, int64_t K, int
     free(z);
   }
   return bad ? -1 : 0;
+}
+
+int orc_quantize_activations(const void* x, int dtype, int64_t M, int64_t K, int norm,
+                             const float* gamma, float eps, int abits, int use_h, int8_t* q, float* deq,
+                             float* rnorm) {
+  return orc_quantize_activations_stat(x, dtype, M, K, norm, gamma, eps, abits, use_h, 0, q, deq, rnorm);
 }
 
 /* ------------------------------------------------------------------------------------
@@ -240,9 +272,9 @@ int orc_dequant(const int32_t* acc, const float* deq, float alpha, int64_t M, in
 /* The whole forward on M rows: quantise activations, integer GEMM, dequantise.
  * T (N*K int8) and alpha come from orc_quantize_weights.  q_out/acc_out/deq_out may be
  * NULL; when given they receive the intermediate results (M*K, M*N, M). */
-int orc_forward(const void* x, int dtype, const int8_t* T, float alpha, int64_t M, int64_t K, int64_t N,
-                int abits, int use_h, int norm, const float* gamma, float eps, float* y, int8_t* q_out,
-                int32_t* acc_out, float* deq_out) {
+int orc_forward_stat(const void* x, int dtype, const int8_t* T, float alpha, int64_t M, int64_t K, int64_t N,
+                     int abits, int use_h, int norm, const float* gamma, float eps, int stat, float* y,
+                     int8_t* q_out, int32_t* acc_out, float* deq_out) {
   if (M < 0 || K <= 0 || N <= 0) return -1;
   if (M == 0) return 0;
   int8_t* q = q_out ? q_out : (int8_t*)malloc((size_t)(M * K));
@@ -250,7 +282,7 @@ int orc_forward(const void* x, int dtype, const int8_t* T, float alpha, int64_t 
   float* deq = deq_out ? deq_out : (float*)malloc((size_t)M * sizeof(float));
   int rc = -1;
   if (q && acc && deq) {
-    rc = orc_quantize_activations(x, dtype, M, K, norm, gamma, eps, abits, use_h, q, deq, NULL);
+    rc = orc_quantize_activations_stat(x, dtype, M, K, norm, gamma, eps, abits, use_h, stat, q, deq, NULL);
     if (rc == 0) rc = orc_gemm_s32(q, T, M, K, N, acc);
     if (rc == 0) rc = orc_dequant(acc, deq, alpha, M, N, y);
   }
@@ -258,6 +290,13 @@ int orc_forward(const void* x, int dtype, const int8_t* T, float alpha, int64_t 
   if (!acc_out) free(acc);
   if (!deq_out) free(deq);
   return rc;
+}
+
+int orc_forward(const void* x, int dtype, const int8_t* T, float alpha, int64_t M, int64_t K, int64_t N,
+                int abits, int use_h, int norm, const float* gamma, float eps, float* y, int8_t* q_out,
+                int32_t* acc_out, float* deq_out) {
+  return orc_forward_stat(x, dtype, T, alpha, M, K, N, abits, use_h, norm, gamma, eps, 0, y, q_out, acc_out,
+                          deq_out);
 }
 
 /* SwiGLU gate of the FFN [V2, section BitNet v2：原生4位激活: RMS normalisation, SwishGLU,

@@ -58,14 +58,14 @@ def _load():
         lib.orc_fwht_f64.argtypes = [P, I64]
         lib.orc_quantize_weights.argtypes = [P, I64, I64, P, P]
         lib.orc_quantize_weights.restype = I
-        lib.orc_quantize_activations.argtypes = [P, I, I64, I64, I, P, Fl, I, I, P, P, P]
-        lib.orc_quantize_activations.restype = I
+        lib.orc_quantize_activations_stat.argtypes = [P, I, I64, I64, I, P, Fl, I, I, I, P, P, P]
+        lib.orc_quantize_activations_stat.restype = I
         lib.orc_gemm_s32.argtypes = [P, P, I64, I64, I64, P]
         lib.orc_gemm_s32.restype = I
         lib.orc_dequant.argtypes = [P, P, Fl, I64, I64, P]
         lib.orc_dequant.restype = I
-        lib.orc_forward.argtypes = [P, I, P, Fl, I64, I64, I64, I, I, I, P, Fl, P, P, P, P]
-        lib.orc_forward.restype = I
+        lib.orc_forward_stat.argtypes = [P, I, P, Fl, I64, I64, I64, I, I, I, P, Fl, I, P, P, P, P]
+        lib.orc_forward_stat.restype = I
         lib.orc_swiglu.argtypes = [P, P, I64, P]
         lib.orc_round_bf16.argtypes = [P, I64, P]
         lib.orc_quantize_qkv.argtypes = [P, I, I64, I64, I, P, P]
@@ -148,16 +148,17 @@ def quantize_weights(W) -> tuple[np.ndarray, float]:
     return T, float(a[0])
 
 
-def quantize_activations(x, abits: int, use_h: bool, norm: bool = False, gamma=None, eps: float = 1e-5):
-    """Returns (q int8 [M,K] unpacked, deq f32 [M], r f32 [M])."""
+def quantize_activations(x, abits: int, use_h: bool, norm: bool = False, gamma=None, eps: float = 1e-5,
+                         stat: int = 0):
+    """Returns (q int8 [M,K] unpacked, deq f32 [M], r f32 [M]).  stat: 0 absmax, 1 absmean."""
     x = np.ascontiguousarray(x)
     M, K = x.shape
     q = np.empty((M, K), np.int8)
     deq = np.empty(M, np.float32)
     r = np.empty(M, np.float32)
     g = None if gamma is None else _c(gamma, np.float32)
-    rc = _load().orc_quantize_activations(_p(x), _xdtype(x), M, K, int(bool(norm)), _p(g), float(eps),
-                                          int(abits), int(bool(use_h)), _p(q), _p(deq), _p(r))
+    rc = _load().orc_quantize_activations_stat(_p(x), _xdtype(x), M, K, int(bool(norm)), _p(g), float(eps),
+                                               int(abits), int(bool(use_h)), int(stat), _p(q), _p(deq), _p(r))
     if rc != 0:
         raise ValueError("orc_quantize_activations: bad arguments")
     return q, deq, r
@@ -185,7 +186,7 @@ def dequant(acc, deq, alpha: float) -> np.ndarray:
 
 
 def forward(x, T, alpha: float, abits: int, use_h: bool, norm: bool = False, gamma=None, eps: float = 1e-5,
-            intermediates: bool = False):
+            intermediates: bool = False, stat: int = 0):
     """Whole forward on the rows of x.  Returns y, or (y, q, acc, deq) with intermediates."""
     x = np.ascontiguousarray(x)
     T = _c(T, np.int8)
@@ -196,8 +197,8 @@ def forward(x, T, alpha: float, abits: int, use_h: bool, norm: bool = False, gam
     acc = np.empty((M, N), np.int32) if intermediates else None
     deq = np.empty(M, np.float32) if intermediates else None
     g = None if gamma is None else _c(gamma, np.float32)
-    rc = _load().orc_forward(_p(x), _xdtype(x), _p(T), float(alpha), M, K, N, int(abits), int(bool(use_h)),
-                             int(bool(norm)), _p(g), float(eps), _p(y), _p(q), _p(acc), _p(deq))
+    rc = _load().orc_forward_stat(_p(x), _xdtype(x), _p(T), float(alpha), M, K, N, int(abits), int(bool(use_h)),
+                                  int(bool(norm)), _p(g), float(eps), int(stat), _p(y), _p(q), _p(acc), _p(deq))
     if rc != 0:
         raise ValueError("orc_forward: bad arguments")
     return (y, q, acc, deq) if intermediates else y

@@ -1,0 +1,64 @@
+"""Pins of the oracle's absmean activation statistic (the INT4 statistic switch).
+
+Hand-derived fixtures (tests/golden/act_quant_absmean.json: ties, clipping at both ends of
+the INT4 range, a zero row), the reconstruction bound |z - q*b| <= b/2 for unclipped
+elements, power-of-two invariance, and the transform + RMSNorm path against an explicit
+fp64 evaluation of the same rule.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from bit_quantized_gemm_bitlinear_amd import inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_absmean_fixture(orc):
+    data = json.load(open(os.path.join(GOLDEN, "act_quant_absmean.json")))
+    for case in data["cases"]:
+        x = np.array([case["x"]], np.float32)
+        q, deq, _ = orc.quantize_activations(x, 4, False, stat=1)
+        assert list(q[0]) == case["q"], case["note"]
+        assert deq[0] == np.float32(case["deq"]), case["note"]
+
+
+@pytest.mark.parametrize("use_h", [False, True])
+def test_absmean_error_bound_and_range(orc, use_h):
+    K = 1024
+    x = inputs.make_activations("mixture", 40, K, outlier_frac=0.01, outlier_scale=50.0, seed=3)
+    q, deq, r = orc.quantize_activations(x, 4, use_h, norm=True, stat=1)
+    assert q.min() >= -8 and q.max() <= 7
+    xf = inputs.bf16_bits_to_f32(x).astype(np.float64)
+    z = orc.fwht_f64(xf) if use_h else xf
+    hK = 1.0 / np.sqrt(K) if use_h else 1.0
+    # b = mean|z| of the unnormalised transform; deq = b * r * hK
+    b = np.abs(z).mean(axis=1)
+    np.testing.assert_allclose(deq, b * r.astype(np.float64) * hK, rtol=1e-5)
+    unclipped = (q > -8) & (q < 7)
+    err = np.abs(z - q * b[:, None])
+    assert (err[unclipped] <= (b[:, None] * np.ones_like(z))[unclipped] * (0.5 + 1e-4)).all()
+    # the codes are the rounded z / b wherever the clip does not bind
+    want = np.clip(np.rint(z / b[:, None]), -8, 7)
+    assert (want != q).mean() < 1e-3          # only fp32-vs-fp64 boundary cases differ
+
+
+def test_absmean_power_of_two_invariance(orc):
+    x = np.random.default_rng(1).standard_normal((8, 256)).astype(np.float32)
+    q1, d1, _ = orc.quantize_activations(x, 4, True, stat=1)
+    q2, d2, _ = orc.quantize_activations(x * np.float32(2.0 ** 9), 4, True, stat=1)
+    np.testing.assert_array_equal(q1, q2)
+    np.testing.assert_array_equal(d2, d1 * np.float32(2.0 ** 9))
+
+
+def test_absmean_forward_composes(orc):
+    wl = inputs.WORKLOADS["wo_1p3b"]
+    x = wl.activations(8)
+    T, a = orc.quantize_weights(wl.weights())
+    y, q, acc, deq = orc.forward(x, T, a, 4, True, norm=True, intermediates=True, stat=1)
+    q2, d2, _ = orc.quantize_activations(x, 4, True, norm=True, stat=1)
+    np.testing.assert_array_equal(q, q2)
+    np.testing.assert_array_equal(deq, d2)
+    np.testing.assert_array_equal(acc, orc.gemm_s32(q, T))
