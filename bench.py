@@ -250,6 +250,39 @@ def main():
             f"{tg6 * 1e6:.1f} us ({g6:.0f} TFLOP/s), outputs identical: {same}")
         del Wq4, ws6, y6
 
+    # ---- the INT4 absmean statistic (the activation-statistic switch), reported beside ----
+    alt_mean = None
+    if abits == 4 and not args.no_alt:
+        def okm(st):
+            if st != 0:
+                raise RuntimeError(L.hbl_last_error().decode())
+
+        def stepm():
+            okm(L.hbl_forward_stat(x.data_ptr(), xt, Wq.data_ptr(), scale.data_ptr(), M, K, N, 4,
+                                   int(wl.use_hadamard), norm, None, 1e-5, B.HBL_STAT_ABSMEAN, y.data_ptr(),
+                                   ws.data_ptr(), ws.numel(), sh))
+
+        for _ in range(args.warmup):
+            stepm()
+        torch.cuda.synchronize()
+        tm = time.perf_counter()
+        for _ in range(args.steps):
+            stepm()
+        torch.cuda.synchronize()
+        elm = time.perf_counter() - tm
+        evm = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_ev)]
+        for i in range(n_ev):
+            evm[i][0].record(stream)
+            okm(L.hbl_quantize_activations_stat(x.data_ptr(), xt, M, K, norm, None, 1e-5, 4, int(wl.use_hadamard),
+                                                B.HBL_STAT_ABSMEAN, codes_view.data_ptr(), deq_view.data_ptr(), sh))
+            evm[i][1].record(stream)
+        torch.cuda.synchronize()
+        tam = sum(e[0].elapsed_time(e[1]) for e in evm) / n_ev * 1e-3
+        alt_mean = {"statistic": "absmean (HBL_STAT_ABSMEAN)", "value": M * args.steps / elm, "unit": "tokens/s",
+                    "ms_per_step": elm * 1e3 / args.steps, "actquant_us": tam * 1e6,
+                    "actquant_gbs": act_bytes / tam / 1e9}
+        log(f"[bench] absmean statistic: {elm * 1e3 / args.steps:.4f} ms/step, act {tam * 1e6:.1f} us")
+
     gemm_kernel = f"k_gemm<{abits}, 256, 256, 2, 4, {256 if abits == 4 else 128}, 1>"
     act_kernel = f"k_actquant_h<{K.bit_length() - 1}, {abits}, 1, 1>"
 
@@ -307,6 +340,7 @@ def main():
                                              "(read x, write packed codes + deq)"},
         "cpu_baseline": cpu,
         "alt_fp6fp4": alt,
+        "alt_absmean": alt_mean,
     }
     print(json.dumps(out), flush=True)
 

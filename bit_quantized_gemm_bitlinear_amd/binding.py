@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(PKG, "libhbl.so")
 HBL_OK, HBL_ERR_INVALID_ARG, HBL_ERR_UNSUPPORTED, HBL_ERR_WORKSPACE, HBL_ERR_HIP = range(5)
 HBL_F32, HBL_BF16 = 0, 1
 HBL_NORM_NONE, HBL_NORM_RMS = 0, 1
+HBL_STAT_ABSMAX, HBL_STAT_ABSMEAN = 0, 1
 
 _lock = threading.Lock()
 _lib = None
@@ -50,6 +51,8 @@ def lib() -> ctypes.CDLL:
             "hbl_forward": (I, [P, I, P, P, I64, I64, I64, I, I, I, P, F, P, P, SZ, P]),
             "hbl_swiglu": (I, [P, P, I64, P, P]),
             "hbl_forward_fused": (I, [I64, I64, I, I]),
+            "hbl_quantize_activations_stat": (I, [P, I, I64, I64, I, P, F, I, I, I, P, P, P]),
+            "hbl_forward_stat": (I, [P, I, P, P, I64, I64, I64, I, I, I, P, F, I, P, P, SZ, P]),
             "hbl_packed_weight_fp4_bytes": (SZ, [I64, I64]),
             "hbl_packed_act_fp6_bytes": (SZ, [I64, I64]),
             "hbl_forward_fp6fp4_workspace_bytes": (SZ, [I64, I64]),
@@ -125,17 +128,18 @@ def quantize_weights(W):
     return Wq, scale
 
 
-def quantize_activations(x, abits: int, use_hadamard: bool, norm: bool = False, gamma=None, eps: float = 1e-5):
-    """x [M, K] bf16/fp32 -> (codes uint8 [M, K*abits/8], deq fp32 [M])."""
+def quantize_activations(x, abits: int, use_hadamard: bool, norm: bool = False, gamma=None, eps: float = 1e-5,
+                         stat: int = HBL_STAT_ABSMAX):
+    """x [M, K] bf16/fp32 -> (codes uint8 [M, K*abits/8], deq fp32 [M]); stat: absmax / absmean."""
     import torch
 
     _dev(x, gamma)
     M, K = x.shape
     codes = torch.empty((M, K * abits // 8), dtype=torch.uint8, device=x.device)
     deq = torch.empty(M, dtype=torch.float32, device=x.device)
-    _check(lib().hbl_quantize_activations(_ptr(x), _xdtype(x), M, K, HBL_NORM_RMS if norm else HBL_NORM_NONE,
-                                          _ptr(gamma), float(eps), int(abits), int(bool(use_hadamard)),
-                                          _ptr(codes), _ptr(deq), _stream()))
+    _check(lib().hbl_quantize_activations_stat(_ptr(x), _xdtype(x), M, K, HBL_NORM_RMS if norm else HBL_NORM_NONE,
+                                               _ptr(gamma), float(eps), int(abits), int(bool(use_hadamard)),
+                                               int(stat), _ptr(codes), _ptr(deq), _stream()))
     return codes, deq
 
 
@@ -170,7 +174,7 @@ def forward_workspace(M: int, K: int, abits: int, device="cuda"):
 
 
 def forward(x, Wq, w_scale, abits: int, use_hadamard: bool, norm: bool = False, gamma=None, eps: float = 1e-5,
-            y=None, ws=None):
+            y=None, ws=None, stat: int = HBL_STAT_ABSMAX):
     """The whole (H-)BitLinear forward: x [M, K] -> y fp32 [M, N]."""
     import torch
 
@@ -181,9 +185,9 @@ def forward(x, Wq, w_scale, abits: int, use_hadamard: bool, norm: bool = False, 
         y = torch.empty((M, N), dtype=torch.float32, device=x.device)
     if ws is None:
         ws = forward_workspace(M, K, abits, x.device)
-    _check(lib().hbl_forward(_ptr(x), _xdtype(x), _ptr(Wq), _ptr(w_scale), M, K, N, int(abits),
-                             int(bool(use_hadamard)), HBL_NORM_RMS if norm else HBL_NORM_NONE, _ptr(gamma),
-                             float(eps), _ptr(y), _ptr(ws), ws.numel(), _stream()))
+    _check(lib().hbl_forward_stat(_ptr(x), _xdtype(x), _ptr(Wq), _ptr(w_scale), M, K, N, int(abits),
+                                  int(bool(use_hadamard)), HBL_NORM_RMS if norm else HBL_NORM_NONE, _ptr(gamma),
+                                  float(eps), int(stat), _ptr(y), _ptr(ws), ws.numel(), _stream()))
     return y
 
 

@@ -217,6 +217,64 @@ hbl_status hbl_forward(const void* x, hbl_dtype xt, const uint8_t* Wq, const flo
   }
 }
 
+hbl_status hbl_quantize_activations_stat(const void* x, hbl_dtype xt, int64_t M, int64_t K, hbl_norm norm,
+                                         const float* gamma, float norm_eps, int abits, int use_hadamard, int stat,
+                                         uint8_t* codes, float* deq, void* stream) {
+  static const char* fn = "hbl_quantize_activations_stat";
+  try {
+    if (stat != HBL_STAT_ABSMAX && stat != HBL_STAT_ABSMEAN) return fail(HBL_ERR_INVALID_ARG, fn, "unknown stat");
+    if (stat == HBL_STAT_ABSMEAN && abits != 4)
+      return fail(HBL_ERR_UNSUPPORTED, fn, "the absmean statistic is implemented for abits = 4");
+    HBL_TRY(check_shape(fn, M, K, -1, abits));
+    HBL_TRY(check_act(fn, xt, norm, gamma, norm_eps, use_hadamard, K));
+    if (M == 0) return HBL_OK;
+    HBL_TRY(check_ptr(fn, x, "x", 16));
+    HBL_TRY(check_ptr(fn, codes, "codes", 16));
+    HBL_TRY(check_ptr(fn, deq, "deq", 4));
+    hipError_t e = hbl::launch_actquant(x, (int)xt, M, K, (int)norm, norm == HBL_NORM_RMS ? gamma : nullptr,
+                                        norm_eps, stat == HBL_STAT_ABSMEAN ? 5 : abits, use_hadamard, codes, deq,
+                                        (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return HBL_OK;
+  } catch (...) {
+    return fail(HBL_ERR_HIP, fn, "unexpected C++ exception");
+  }
+}
+
+hbl_status hbl_forward_stat(const void* x, hbl_dtype xt, const uint8_t* Wq, const float* w_scale, int64_t M,
+                            int64_t K, int64_t N, int abits, int use_hadamard, hbl_norm norm, const float* gamma,
+                            float norm_eps, int stat, float* y, void* ws, size_t ws_bytes, void* stream) {
+  static const char* fn = "hbl_forward_stat";
+  try {
+    if (stat == HBL_STAT_ABSMAX)
+      return hbl_forward(x, xt, Wq, w_scale, M, K, N, abits, use_hadamard, norm, gamma, norm_eps, y, ws, ws_bytes,
+                         stream);
+    if (stat != HBL_STAT_ABSMEAN) return fail(HBL_ERR_INVALID_ARG, fn, "unknown stat");
+    if (abits != 4) return fail(HBL_ERR_UNSUPPORTED, fn, "the absmean statistic is implemented for abits = 4");
+    HBL_TRY(check_shape(fn, M, K, N, abits));
+    HBL_TRY(check_act(fn, xt, norm, gamma, norm_eps, use_hadamard, K));
+    HBL_TRY(check_ptr(fn, Wq, "Wq", 16));
+    HBL_TRY(check_ptr(fn, w_scale, "w_scale", 4));
+    if (M == 0) return HBL_OK;
+    HBL_TRY(check_ptr(fn, x, "x", 16));
+    HBL_TRY(check_ptr(fn, y, "y", 16));
+    if (ws == nullptr || ws_bytes < hbl_forward_workspace_bytes(M, K, abits))
+      return fail(HBL_ERR_WORKSPACE, fn, "workspace missing or smaller than hbl_forward_workspace_bytes");
+    HBL_TRY(check_ptr(fn, ws, "ws", 256));
+    uint8_t* codes = static_cast<uint8_t*>(ws);
+    float* deq = reinterpret_cast<float*>(codes + round256((size_t)(M * K * abits / 8)));
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = hbl::launch_actquant(x, (int)xt, M, K, (int)norm, norm == HBL_NORM_RMS ? gamma : nullptr,
+                                        norm_eps, 5, use_hadamard, codes, deq, s);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    e = hbl::launch_gemm(codes, deq, Wq, w_scale, M, K, N, 4, nullptr, y, s);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return HBL_OK;
+  } catch (...) {
+    return fail(HBL_ERR_HIP, fn, "unexpected C++ exception");
+  }
+}
+
 size_t hbl_packed_weight_fp4_bytes(int64_t N, int64_t K) {
   if (N < 1 || K < 64 || K % 64 != 0 || K > HBL_MAX_K || N > INT32_MAX) return 0;
   return (size_t)(N * (K / 2));

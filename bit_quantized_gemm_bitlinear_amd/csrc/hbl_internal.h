@@ -12,7 +12,8 @@ hipError_t launch_wquant(const float* W, int64_t N, int64_t K, uint8_t* Wq, floa
                          hipStream_t s);
 
 // Activation quantisation (k_actquant.hip).  xt: 0 fp32, 1 bf16.  abits: 4 (INT4 nibbles),
-// 8 (INT8) or 6 (INT4 values stored as FP6 E2M3 codes).
+// 8 (INT8), 6 (INT4 values stored as FP6 E2M3 codes) or 5 (INT4 nibbles with the absmean
+// statistic).
 hipError_t launch_actquant(const void* x, int xt, int64_t M, int64_t K, int norm, const float* gamma,
                            float eps, int abits, int use_h, uint8_t* codes, float* deq, hipStream_t s);
 

@@ -118,14 +118,16 @@ __device__ __forceinline__ double row_sum(double v, double* red) {
 }
 
 // ABITS: 4 = INT4 codes packed as nibbles, 8 = INT8 codes, 6 = INT4 codes (Qb = 7) stored as
-// FP6 E2M3 (6 bits each, code k at bits [6k, 6k+6) of the row's little-endian bit string).
+// FP6 E2M3 (6 bits each, code k at bits [6k, 6k+6) of the row's little-endian bit string),
+// 5 = INT4 codes packed as nibbles with the absmean statistic instead of absmax:
+// b = mean|z| (fp64 sum), s = fl32(1/b), q = clamp(rint(z*s), -8, 7), deq = b*r*hK.
 template <int ABITS>
 struct QB {
   static constexpr float value = ABITS == 8 ? 127.0f : 7.0f;
 };
 
 template <int ABITS>
-constexpr int row_bytes(int K) { return ABITS == 4 ? K / 2 : (ABITS == 8 ? K : K * 6 / 8); }
+constexpr int row_bytes(int K) { return (ABITS == 4 || ABITS == 5) ? K / 2 : (ABITS == 8 ? K : K * 6 / 8); }
 
 typedef float v16f_t __attribute__((ext_vector_type(16)));
 
@@ -197,15 +199,18 @@ __device__ __forceinline__ void store_run(const float* v, float s, uint8_t* __re
         d16[2] = (uint16_t)(w[1] & 0xffffu);
       }
     }
-  } else if constexpr (ABITS == 4) {
+  } else if constexpr (ABITS == 4 || ABITS == 5) {
+    // absmean codes can exceed the INT4 range: clamp before rounding (same as after, the
+    // bounds being integers)
+    auto sc = [&](float z) { return ABITS == 5 ? fminf(fmaxf(z * s, -8.0f), 7.0f) : z * s; };
     uint32_t w[RL / 8];
 #pragma unroll
     for (int d = 0; d < RL / 8; ++d) {
       uint32_t b[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint32_t lo = rne_bits(v[8 * d + i] * s, MAGIC + 8.0f);
-        const uint32_t hi = rne_bits(v[8 * d + i + 4] * s, MAGIC + 8.0f);
+        const uint32_t lo = rne_bits(sc(v[8 * d + i]), MAGIC + 8.0f);
+        const uint32_t hi = rne_bits(sc(v[8 * d + i + 4]), MAGIC + 8.0f);
         b[i] = (hi << 4) | lo;  // byte 0 = (hi+8) << 4 | (lo+8); higher bytes unused
       }
       const uint32_t b01 = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u);
@@ -362,12 +367,20 @@ __global__ __launch_bounds__(block_threads<L>()) void k_actquant_h(
     }
 
     float amax = 0.0f;
+    if constexpr (ABITS == 5) {
+      double sa = 0.0;
 #pragma unroll
-    for (int j = 0; j < 64; ++j) amax = fmaxf(amax, fabsf(v[j]));
-    amax = row_max<T>(amax, redf);
+      for (int j = 0; j < 64; ++j) sa += (double)fabsf(v[j]);
+      amax = (float)(row_sum<T>(sa, redd) / (double)K);  // the absmean statistic b
+    } else {
+#pragma unroll
+      for (int j = 0; j < 64; ++j) amax = fmaxf(amax, fabsf(v[j]));
+      amax = row_max<T>(amax, redf);
+    }
 
     const bool zero = amax < 0x1p-120f;     // also keeps Qb / amax finite
-    const float s = zero ? 0.0f : Qb / amax;  // s = 0 quantises the whole row to 0
+    // s = 0 quantises the whole row to 0
+    const float s = zero ? 0.0f : (ABITS == 5 ? 1.0f / amax : Qb / amax);
     if (valid) {
       uint8_t* crow = codes + row * (int64_t)row_bytes<ABITS>(K);
       constexpr int LASTP = NP - 1;
@@ -377,7 +390,8 @@ __global__ __launch_bounds__(block_threads<L>()) void k_actquant_h(
 #pragma unroll
       for (int gi = 0; gi < 64 / RL; ++gi)
         store_run<ABITS, RL>(v + gi * RL, s, crow, NP == 1 ? b + gi * RL : b + LY::off(gi * RL));
-      if (t == 0) deq[row] = zero ? 0.0f : __fmul_rn(__fmul_rn(amax / Qb, r), hK);
+      if (t == 0)
+        deq[row] = zero ? 0.0f : __fmul_rn(__fmul_rn(ABITS == 5 ? amax : amax / Qb, r), hK);
     }
     cur = nxt;
     // The next group reuses LDS and the reduction slots: every thread must be done with them.
@@ -603,6 +617,7 @@ __global__ __launch_bounds__(256) void k_actquant_plain(const void* __restrict__
   constexpr int NCHR = NCH > 0 ? NCH : 1;
   __shared__ float redf[4];
   __shared__ double redd[4];
+  __shared__ double redd2[4];
   const int64_t row = blockIdx.x;
   const int tid = threadIdx.x;
   const int nch = (int)(K / 8);
@@ -625,7 +640,7 @@ __global__ __launch_bounds__(256) void k_actquant_plain(const void* __restrict__
     }
   };
   float v[NCHR][8];
-  double ss = 0.0;
+  double ss = 0.0, sa = 0.0;  // sa: sum |u| for the absmean statistic (ABITS 5)
   float amax = 0.0f;
   if constexpr (NCH > 0) {
 #pragma unroll
@@ -639,7 +654,10 @@ __global__ __launch_bounds__(256) void k_actquant_plain(const void* __restrict__
         }
         scale8(ch, v[c]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[c][e]));
+        for (int e = 0; e < 8; ++e) {
+          if constexpr (ABITS == 5) sa += (double)fabsf(v[c][e]);
+          else amax = fmaxf(amax, fabsf(v[c][e]));
+        }
       }
     }
   } else {
@@ -652,7 +670,10 @@ __global__ __launch_bounds__(256) void k_actquant_plain(const void* __restrict__
       }
       scale8(ch, o);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(o[e]));
+      for (int e = 0; e < 8; ++e) {
+        if constexpr (ABITS == 5) sa += (double)fabsf(o[e]);
+        else amax = fmaxf(amax, fabsf(o[e]));
+      }
     }
   }
   float r = 1.0f;
@@ -660,18 +681,21 @@ __global__ __launch_bounds__(256) void k_actquant_plain(const void* __restrict__
     ss = row_sum<256>(ss, redd);
     r = (float)(1.0 / sqrt(ss / (double)K + (double)eps));
   }
-  amax = row_max<256>(amax, redf);
+  if constexpr (ABITS == 5) amax = (float)(row_sum<256>(sa, redd2) / (double)K);  // the absmean b
+  else amax = row_max<256>(amax, redf);
   constexpr float Qb = QB<ABITS>::value;
   const bool zero = amax < 0x1p-120f;
-  const float s = zero ? 0.0f : Qb / amax;
+  const float s = zero ? 0.0f : (ABITS == 5 ? 1.0f / amax : Qb / amax);
   uint8_t* crow = codes + row * (int64_t)row_bytes<ABITS>((int)K);
   auto put = [&](int ch, const float* o) {
     if constexpr (ABITS == 6) {
       store_run<6, 8>(o, s, crow, 8 * ch);
-    } else if constexpr (ABITS == 4) {
+    } else if constexpr (ABITS == 4 || ABITS == 5) {
+      auto q = [&](float z) {  // absmean codes can exceed the INT4 range
+        return ABITS == 5 ? rne_int(fminf(fmaxf(z * s, -8.0f), 7.0f)) : rne_int(z * s);
+      };
       *reinterpret_cast<uint32_t*>(crow + 4 * ch) =
-          pack8_a4(rne_int(o[0] * s), rne_int(o[1] * s), rne_int(o[2] * s), rne_int(o[3] * s),
-                   rne_int(o[4] * s), rne_int(o[5] * s), rne_int(o[6] * s), rne_int(o[7] * s));
+          pack8_a4(q(o[0]), q(o[1]), q(o[2]), q(o[3]), q(o[4]), q(o[5]), q(o[6]), q(o[7]));
     } else {
       *reinterpret_cast<uint2*>(crow + 8 * ch) =
           make_uint2(pack4_a8(rne_int(o[0] * s), rne_int(o[1] * s), rne_int(o[2] * s), rne_int(o[3] * s)),
@@ -692,7 +716,7 @@ __global__ __launch_bounds__(256) void k_actquant_plain(const void* __restrict__
       put(ch, o);
     }
   }
-  if (tid == 0) deq[row] = zero ? 0.0f : __fmul_rn(amax / Qb, r);
+  if (tid == 0) deq[row] = zero ? 0.0f : __fmul_rn(ABITS == 5 ? amax : amax / Qb, r);
 }
 
 template <int L, int ABITS, int XT>
@@ -788,6 +812,9 @@ hipError_t launch_actquant(const void* x, int xt, int64_t M, int64_t K, int norm
     if (abits == 6)
       return xt ? dispatch_h<6, 1>(L, x, M, gamma, eps, norm, codes, deq, s)
                 : dispatch_h<6, 0>(L, x, M, gamma, eps, norm, codes, deq, s);
+    if (abits == 5)
+      return xt ? dispatch_h<5, 1>(L, x, M, gamma, eps, norm, codes, deq, s)
+                : dispatch_h<5, 0>(L, x, M, gamma, eps, norm, codes, deq, s);
     return xt ? dispatch_h<8, 1>(L, x, M, gamma, eps, norm, codes, deq, s)
               : dispatch_h<8, 0>(L, x, M, gamma, eps, norm, codes, deq, s);
   }
@@ -797,6 +824,9 @@ hipError_t launch_actquant(const void* x, int xt, int64_t M, int64_t K, int norm
   if (abits == 6)
     return xt ? dispatch_plain<6, 1>(x, M, K, gamma, eps, norm, codes, deq, s)
               : dispatch_plain<6, 0>(x, M, K, gamma, eps, norm, codes, deq, s);
+  if (abits == 5)
+    return xt ? dispatch_plain<5, 1>(x, M, K, gamma, eps, norm, codes, deq, s)
+              : dispatch_plain<5, 0>(x, M, K, gamma, eps, norm, codes, deq, s);
   return xt ? dispatch_plain<8, 1>(x, M, K, gamma, eps, norm, codes, deq, s)
             : dispatch_plain<8, 0>(x, M, K, gamma, eps, norm, codes, deq, s);
 }

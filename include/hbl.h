@@ -107,6 +107,8 @@ typedef enum {
 
 typedef enum { HBL_F32 = 0, HBL_BF16 = 1 } hbl_dtype;
 typedef enum { HBL_NORM_NONE = 0, HBL_NORM_RMS = 1 } hbl_norm;
+/* Per-token activation statistic (see hbl_quantize_activations_stat). */
+typedef enum { HBL_STAT_ABSMAX = 0, HBL_STAT_ABSMEAN = 1 } hbl_stat;
 
 /* Limits of this implementation.
  *  K % 64 == 0 and 64 <= K <= HBL_MAX_K for every call.
@@ -167,6 +169,24 @@ hbl_status hbl_forward(const void* x, hbl_dtype xt, const uint8_t* Wq, const flo
                        int64_t K, int64_t N, int abits, int use_hadamard, hbl_norm norm,
                        const float* gamma, float norm_eps, float* y, void* ws, size_t ws_bytes,
                        void* stream);
+
+/* The activation statistic switch.  The write-up (section H-BitLinear模塊) says INT8 and INT4
+ * activations use different strategies and drops both equations; HBL_STAT_ABSMAX (the
+ * default of every other call) is the reading above, HBL_STAT_ABSMEAN the alternative for
+ * INT4: the absmean function the pages give for the weights (scale by the mean absolute
+ * value, round to the nearest integer, clip) on the INT4 grid:
+ *     b = (float)((sum_k |z_k|, fp64) / K); if b < 2^-120: q = 0, deq = 0
+ *     else: s = fl32(1 / b);  q = clamp(rint_ne(fl32(z * s)), -8, 7);  deq = fl32(fl32(b * r) * hK)
+ * Codes, packing and the GEMM are unchanged.  HBL_STAT_ABSMEAN needs abits = 4
+ * (HBL_ERR_UNSUPPORTED otherwise).  The sum's order on the GPU differs from ascending; b can
+ * differ from the ascending-order value by one ulp in rare rows (about 1e-5 of rows), which
+ * moves codes at rounding boundaries. */
+hbl_status hbl_quantize_activations_stat(const void* x, hbl_dtype xt, int64_t M, int64_t K, hbl_norm norm,
+                                         const float* gamma, float norm_eps, int abits, int use_hadamard, int stat,
+                                         uint8_t* codes, float* deq, void* stream);
+hbl_status hbl_forward_stat(const void* x, hbl_dtype xt, const uint8_t* Wq, const float* w_scale, int64_t M,
+                            int64_t K, int64_t N, int abits, int use_hadamard, hbl_norm norm, const float* gamma,
+                            float norm_eps, int stat, float* y, void* ws, size_t ws_bytes, void* stream);
 
 /* 1 if hbl_forward(M, K, ..., abits, use_hadamard) runs as one fused kernel, else 0.  With a
  * few token rows (use_hadamard, K = 4096 .. 16384, M <= 256 / (K / 64)), each block of the

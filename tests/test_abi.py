@@ -258,3 +258,14 @@ def test_forward_fused_query(L):
     assert L.hbl_forward_fused(1, 16384, 4, 0) == 0
     assert L.hbl_forward_fused(0, 16384, 4, 1) == 0
     assert L.hbl_forward_fused(1, 12288, 4, 1) == 0
+
+
+def test_stat_rejects(L):
+    q = L.hbl_quantize_activations_stat
+    assert q(FAKE, 1, 4, 256, 0, None, 1e-5, 4, 1, 2, FAKE, FAKE, S) == B.HBL_ERR_INVALID_ARG      # unknown stat
+    assert q(FAKE, 1, 4, 256, 0, None, 1e-5, 8, 1, 1, FAKE, FAKE, S) == B.HBL_ERR_UNSUPPORTED      # absmean needs a4
+    assert q(None, 1, 0, 256, 0, None, 1e-5, 4, 1, 1, None, None, S) == B.HBL_OK
+    f = L.hbl_forward_stat
+    assert f(FAKE, 1, FAKE, FAKE, 4, 256, 8, 4, 1, 1, None, 1e-5, 3, FAKE, FAKE, 1 << 20, S) == B.HBL_ERR_INVALID_ARG
+    assert f(FAKE, 1, FAKE, FAKE, 4, 256, 8, 8, 1, 1, None, 1e-5, 1, FAKE, FAKE, 1 << 20, S) == B.HBL_ERR_UNSUPPORTED
+    assert f(FAKE, 1, FAKE, FAKE, 4, 256, 8, 4, 1, 1, None, 1e-5, 1, FAKE, FAKE, 10, S) == B.HBL_ERR_WORKSPACE
