@@ -497,19 +497,22 @@ def bench_decode(args, wl):
             step(i)
         torch.cuda.synchronize()
         el = (time.perf_counter() - t0) / steps
-        # per-kernel durations with HIP events on the launch stream
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        # per-kernel durations: HIP events on the launch stream around `steps` back-to-back
+        # launches of each kernel (an event pair per launch would add its own few microseconds
+        # to kernels this short)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        ev[0].record(stream)
         for i in range(steps):
-            ev[i][0].record(stream)
             ok(L.hbl_quantize_activations(x.data_ptr(), B.HBL_BF16, M, K, B.HBL_NORM_RMS, None, 1e-5, 4, 1,
                                           codes.data_ptr(), deq.data_ptr(), sh))
-            ev[i][1].record(stream)
+        ev[1].record(stream)
+        for i in range(steps):
             ok(L.hbl_gemm_dequant(codes.data_ptr(), deq.data_ptr(), Wqs[i % copies].data_ptr(), scale.data_ptr(), M,
                                   K, N, 4, y.data_ptr(), sh))
-            ev[i][2].record(stream)
+        ev[2].record(stream)
         torch.cuda.synchronize()
-        t_act = sum(e[0].elapsed_time(e[1]) for e in ev) / steps * 1e-3
-        t_gemv = sum(e[1].elapsed_time(e[2]) for e in ev) / steps * 1e-3
+        t_act = ev[0].elapsed_time(ev[1]) / steps * 1e-3
+        t_gemv = ev[1].elapsed_time(ev[2]) / steps * 1e-3
         gemv_bytes = N * K // 4 + M * K // 2 + 4 * M + 4 + 4 * M * N
         fused = bool(L.hbl_forward_fused(M, K, 4, 1))
         per[M] = {"us_per_step": el * 1e6, "tokens_per_s": M / el,
