@@ -283,7 +283,7 @@ def main():
                     "actquant_gbs": act_bytes / tam / 1e9}
         log(f"[bench] absmean statistic: {elm * 1e3 / args.steps:.4f} ms/step, act {tam * 1e6:.1f} us")
 
-    gemm_kernel = f"k_gemm<{abits}, 256, 256, 2, 4, {256 if abits == 4 else 128}, 1>"
+    gemm_kernel = f"k_gemm<{abits}, 256, 256, 2, 4, {256 if abits == 4 else 128}, 1, {'true' if K % (256 if abits == 4 else 128) == 0 else 'false'}>"
     act_kernel = f"k_actquant_h<{K.bit_length() - 1}, {abits}, 1, 1>"
 
     # ---- CPU oracle baseline on a bounded sample of rows ----
@@ -441,7 +441,7 @@ def bench_ffn(args, wl):
            "parts_us": {name: v for (name, _), v in zip(parts, sums)},
            "roofline": {"bound": "mfma", "achieved": gu_tops, "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
                         "frac": gu_tops / PEAK_INT8_TOPS,
-                        "traffic": measured_traffic("k_gemm<4, 256, 256, 2, 4, 256, 3>"),
+                        "traffic": measured_traffic("k_gemm<4, 256, 256, 2, 4, 256, 3, true>"),
                         "traffic_unit": "HBM-side bytes per launch (FETCH_SIZE x2.0 + WRITE_SIZE x1.0)",
                         "kernel": "k_gemm fused gate/up + SwiGLU epilogue (v_mfma_i32_32x32x32_i8)",
                         "algorithmic": "2*M*(2*ffn)*hidden int8 ops per launch"}}
