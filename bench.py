@@ -33,6 +33,11 @@ METRIC = "H-BitLinear a4 tokens/s + effective TOPS (% int8 MFMA peak), 7B-like W
 PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, 5.0 POP/s
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
 PEAK_FP4_TFLOPS = 10100.0    # MI355X dense FP6 / FP4 MFMA, 10.1 PFLOP/s
+# fp32 vector adds: 157.3 TFLOP/s counts an FMA as two flops, so 78.6 T adds/s (packed, two per
+# lane per clock: 256 CUs x 64 lanes x 2 x 2.4 GHz).  Code built without packed fp32, as
+# this library is, issues at most half of that: 39.3 T adds/s.
+PEAK_FP32_ADD_TOPS = 78.6
+NONPACKED_FP32_ADD_TOPS = 39.3
 
 
 def log(*a):
@@ -283,8 +288,22 @@ def main():
                     "actquant_gbs": act_bytes / tam / 1e9}
         log(f"[bench] absmean statistic: {elm * 1e3 / args.steps:.4f} ms/step, act {tam * 1e6:.1f} us")
 
+    # The activation kernel with the transform is bound by its fp32 butterflies (K log2 K adds
+    # per token), not by HBM; without the transform it streams.
+    act_hbm = {"achieved": act_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": act_gbs / PEAK_HBM_GBS,
+               "algorithmic": f"{act_bytes_per_token(K, abits, x_bytes)} B per token (read x, write packed codes + deq)"}
+    if wl.use_hadamard:
+        fwht_tops = M * K * (K.bit_length() - 1) / t_act / 1e12
+        act_roofline = {"bound": "alu", "achieved": fwht_tops, "peak": PEAK_FP32_ADD_TOPS, "unit": "Tops/s",
+                        "frac": fwht_tops / PEAK_FP32_ADD_TOPS,
+                        "algorithmic": f"K*log2(K) = {K * (K.bit_length() - 1)} fp32 butterfly add/sub per token",
+                        "peak_nonpacked": NONPACKED_FP32_ADD_TOPS, "hbm": act_hbm}
+    else:
+        act_roofline = {"bound": "hbm", **act_hbm}
+    act_roofline["traffic_unit"] = "HBM-side bytes per launch (FETCH_SIZE x2.0 + WRITE_SIZE x1.0)"
     gemm_kernel = f"k_gemm<{abits}, 256, 256, 2, 4, {256 if abits == 4 else 128}, 1, {'true' if K % (256 if abits == 4 else 128) == 0 else 'false'}>"
     act_kernel = f"k_actquant_h<{K.bit_length() - 1}, {abits}, 1, 1>"
+    act_roofline["traffic"] = measured_traffic(act_kernel) if wl.name == "wdown_7b" else None
 
     # ---- CPU oracle baseline on a bounded sample of rows ----
     cpu = None
@@ -332,12 +351,7 @@ def main():
                      "traffic_unit": "HBM-side bytes per launch (FETCH_SIZE x2.0 + WRITE_SIZE x1.0)",
                      "kernel": "k_gemm (ternary x INT%d, v_mfma_i32_32x32x32_i8)" % abits,
                      "algorithmic": "2*M*N*K int8 ops per launch"},
-        "roofline_actquant": {"bound": "hbm", "achieved": act_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                              "frac": act_gbs / PEAK_HBM_GBS,
-                              "traffic": measured_traffic(act_kernel) if wl.name == "wdown_7b" else None,
-                              "traffic_unit": "HBM-side bytes per launch (FETCH_SIZE x2.0 + WRITE_SIZE x1.0)",
-                              "algorithmic": f"{act_bytes_per_token(K, abits, x_bytes)} B per token "
-                                             "(read x, write packed codes + deq)"},
+        "roofline_actquant": act_roofline,
         "cpu_baseline": cpu,
         "alt_fp6fp4": alt,
         "alt_absmean": alt_mean,
