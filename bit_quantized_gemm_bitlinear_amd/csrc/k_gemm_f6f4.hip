@@ -16,8 +16,13 @@
 // accumulators per lane, two waves per SIMD).  FP6/FP4 fragments are larger per MFMA than the
 // int8 path's packed INT4/2-bit fragments (40 bytes per lane per 64-deep step), so LDS and L2
 // traffic per MFMA is higher; the wave shape keeps A (the larger operand) read by only two
-// waves.  K is staged through double-buffered LDS 128 deep; see the main loop for the
-// software pipeline.
+// waves.  K is staged through double-buffered LDS 128 deep.  A stage is short in time (two
+// 64-deep MFMA steps), so global loads are issued two stages ahead into one of two register
+// sets; with loads one stage ahead the waves waited on memory for most of each stage.  When
+// K is a multiple of the stage depth the loads carry no K-tail masks.  See the main loop for
+// the software pipeline.
+#include <type_traits>
+
 #include "hbl_device.h"
 #include "hbl_internal.h"
 
@@ -42,7 +47,7 @@ __device__ __forceinline__ void tile_order(int bid, int nblk, int ntm, int ntn, 
   tn = r / gm;
 }
 
-template <int BM, int BN, int WR, int WC, int MODE>
+template <int BM, int BN, int WR, int WC, int MODE, bool FULLK>
 __global__ __launch_bounds__(64 * WR * WC) void k_gemm_f6f4(const uint8_t* __restrict__ A,
                                                             const float* __restrict__ deq,
                                                             const uint8_t* __restrict__ B,
@@ -89,13 +94,39 @@ __global__ __launch_bounds__(64 * WR * WC) void k_gemm_f6f4(const uint8_t* __res
     boff[i] = (uint32_t)(min(r, N - 1 - n0) * brow + 16 * c);
   }
 
-  uint4 ra[ALD], rb[BLD];
+  // Two register sets stage the global loads: set S receives stage kt + 2 while the other set,
+  // loaded a stage earlier, is stored to LDS.  S is a compile-time constant at every call;
+  // the sets are chosen with if constexpr and copied element by element, because a run-time
+  // subscript or pointer select on them makes the compiler keep them in memory (it then
+  // moves them into LDS).
+  struct Stage {
+    uint4 a[ALD], b[BLD];
+  };
+  Stage st0, st1;
+  auto stg = [&](auto S) __attribute__((always_inline)) -> Stage& {
+    if constexpr (decltype(S)::value == 0) return st0;
+    else return st1;
+  };
   // Stage kt; in a partial last stage only the first n64 64-deep slices exist and the rest
   // is zero-filled (a zero FP4 weight contributes nothing).
-  auto gload = [&](int kt, int n64) {
-    const int va = n64 * 48 / 16, vb = n64 * 32 / 16;
+  auto gload = [&](auto S, int kt, int n64) __attribute__((always_inline)) {
+    Stage& r = stg(S);
     const uint8_t* ak = Ablk + (int64_t)kt * AB;
     const uint8_t* bk = Bblk + (int64_t)kt * BB;
+    if constexpr (FULLK) {  // K a multiple of the stage depth: every chunk exists
+#pragma unroll
+      for (int i = 0; i < ALD; ++i) {
+        const uint4 v = *reinterpret_cast<const uint4*>(ak + aoff[i]);
+        r.a[i] = make_uint4(v.x, v.y, v.z, v.w);
+      }
+#pragma unroll
+      for (int i = 0; i < BLD; ++i) {
+        const uint4 v = *reinterpret_cast<const uint4*>(bk + boff[i]);
+        r.b[i] = make_uint4(v.x, v.y, v.z, v.w);
+      }
+      return;
+    }
+    const int va = n64 * 48 / 16, vb = n64 * 32 / 16;
     // Chunks past the end are loaded from the last valid chunk of their row (always in
     // bounds) and cleared with a mask the compiler cannot see through, so the loads stay
     // unconditional and the loop body stays one basic block.
@@ -105,7 +136,7 @@ __global__ __launch_bounds__(64 * WR * WC) void k_gemm_f6f4(const uint8_t* __res
       uint32_t keep = c < va ? ~0u : 0u;
       asm volatile("" : "+v"(keep));
       const uint4 v = *reinterpret_cast<const uint4*>(ak + aoff[i] - back);
-      ra[i] = make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
+      r.a[i] = make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
     }
 #pragma unroll
     for (int i = 0; i < BLD; ++i) {
@@ -113,21 +144,23 @@ __global__ __launch_bounds__(64 * WR * WC) void k_gemm_f6f4(const uint8_t* __res
       uint32_t keep = c < vb ? ~0u : 0u;
       asm volatile("" : "+v"(keep));
       const uint4 v = *reinterpret_cast<const uint4*>(bk + boff[i] - back);
-      rb[i] = make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
+      r.b[i] = make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
     }
   };
-  auto swrite = [&](int buf) {
+  auto swrite = [&](auto S, int buf) __attribute__((always_inline)) {
+    const Stage& r = stg(S);
 #pragma unroll
     for (int i = 0; i < ALD; ++i) {
       const int e = tid + NT * i;
       uint8_t* d = &sA[buf][(e / ACH) * AS + 16 * (e % ACH)];
-      reinterpret_cast<uint2*>(d)[0] = make_uint2(ra[i].x, ra[i].y);
-      reinterpret_cast<uint2*>(d)[1] = make_uint2(ra[i].z, ra[i].w);
+      reinterpret_cast<uint2*>(d)[0] = make_uint2(r.a[i].x, r.a[i].y);
+      reinterpret_cast<uint2*>(d)[1] = make_uint2(r.a[i].z, r.a[i].w);
     }
 #pragma unroll
     for (int i = 0; i < BLD; ++i) {
       const int e = tid + NT * i;
-      *reinterpret_cast<uint4*>(&sB[buf][(e / BCH) * BS + 16 * (e % BCH)]) = rb[i];
+      *reinterpret_cast<uint4*>(&sB[buf][(e / BCH) * BS + 16 * (e % BCH)]) =
+          make_uint4(r.b[i].x, r.b[i].y, r.b[i].z, r.b[i].w);
     }
   };
 
@@ -169,23 +202,24 @@ __global__ __launch_bounds__(64 * WR * WC) void k_gemm_f6f4(const uint8_t* __res
     }
   };
 
-  // Software pipeline over two LDS buffers: the global loads of stage kt + 1 are issued at
-  // the start of stage kt and stored into the other buffer during its second k-step, and the
-  // fragments of each k-step are read during the MFMAs of the previous one.  The loop body
-  // has no branches (the last stage reloads itself into the idle buffer), so it is one
-  // scheduling region, and the group barriers interleave one memory instruction after each
-  // MFMA.  Two waves share each SIMD, so one wave's barrier or load wait is covered by the
-  // other's MFMAs.
+  // Software pipeline over two LDS buffers and two register sets: the global loads of stage
+  // kt + 2 are issued at the start of stage kt, and stage kt + 1 (loaded during stage kt - 1)
+  // is stored into the other LDS buffer during kt's second k-step, so a load has about one
+  // and a half stages to arrive; the fragments of each k-step are read during the MFMAs of
+  // the previous one.  A stage has no branches (loads past the last stage reload the last
+  // one, and what they store goes to the idle buffer), so it is one scheduling region, and
+  // the group barriers interleave one memory instruction after each MFMA.  Two waves share
+  // each SIMD, so one wave's barrier or load wait is covered by the other's MFMAs.
   constexpr int NMF = TM * TN;                 // MFMAs per k-step
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
   Frag f0, f1;
-  gload(0, KT == 1 ? last_k64 : KS);
-  swrite(0);
-  __syncthreads();
-  fread(0, 0, f0);
-  for (int kt = 0; kt < KT; ++kt) {
+  // One stage; S is the register set that receives stage kt + 2.
+  auto stage = [&](auto S, int kt) __attribute__((always_inline)) {
+    constexpr int set = decltype(S)::value;
     const int buf = kt & 1;
-    const int nx = kt + 1 < KT ? kt + 1 : kt;
-    gload(nx, nx == KT - 1 ? last_k64 : KS);
+    const int nx = min(kt + 2, KT - 1);
+    gload(S, nx, nx == KT - 1 ? last_k64 : KS);
     fread(buf, 1, f1);
     fmma(f0);
 #pragma unroll
@@ -194,7 +228,7 @@ __global__ __launch_bounds__(64 * WR * WC) void k_gemm_f6f4(const uint8_t* __res
       if (i < ALD + BLD) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one global load
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
     }
-    swrite(buf ^ 1);
+    swrite(std::integral_constant<int, 1 - set>{}, buf ^ 1);
     fmma(f1);
 #pragma unroll
     for (int i = 0; i < NMF; ++i) {
@@ -203,7 +237,19 @@ __global__ __launch_bounds__(64 * WR * WC) void k_gemm_f6f4(const uint8_t* __res
     }
     __syncthreads();
     fread(buf ^ 1, 0, f0);
+  };
+  gload(I0{}, 0, KT == 1 ? last_k64 : KS);
+  const int n1 = min(1, KT - 1);
+  gload(I1{}, n1, n1 == KT - 1 ? last_k64 : KS);
+  swrite(I0{}, 0);
+  __syncthreads();
+  fread(0, 0, f0);
+  int kt = 0;
+  for (; kt + 1 < KT; kt += 2) {
+    stage(I0{}, kt);
+    stage(I1{}, kt + 1);
   }
+  if (kt < KT) stage(I0{}, kt);
 
   float alpha = 0.0f;
   if constexpr (MODE == 1) alpha = w_scale[0];
@@ -234,8 +280,12 @@ template <int BM, int BN, int WR, int WC, int MODE>
 hipError_t launch_cfg(const uint8_t* codes, const float* deq, const uint8_t* Wq4, const float* w_scale, int64_t M,
                       int64_t K, int64_t N, int32_t* acc, float* y, hipStream_t s) {
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  hipLaunchKernelGGL((k_gemm_f6f4<BM, BN, WR, WC, MODE>), dim3((unsigned)tiles), dim3(64 * WR * WC), 0, s, codes,
-                     deq, Wq4, w_scale, (int)M, (int)N, (int)K, acc, y);
+  if (K % BK6 == 0)
+    hipLaunchKernelGGL((k_gemm_f6f4<BM, BN, WR, WC, MODE, true>), dim3((unsigned)tiles), dim3(64 * WR * WC), 0, s,
+                       codes, deq, Wq4, w_scale, (int)M, (int)N, (int)K, acc, y);
+  else
+    hipLaunchKernelGGL((k_gemm_f6f4<BM, BN, WR, WC, MODE, false>), dim3((unsigned)tiles), dim3(64 * WR * WC), 0, s,
+                       codes, deq, Wq4, w_scale, (int)M, (int)N, (int)K, acc, y);
   return hipGetLastError();
 }
 
