@@ -61,3 +61,19 @@ def test_absmean_forward_7b_rows(orc):
     y = to_host(B.forward(to_dev(x), Wq, scale, 4, True, norm=True, stat=B.HBL_STAT_ABSMEAN))
     y_o = orc.forward(x, T, alpha, 4, True, norm=True, stat=1)
     assert rel_fro(y, y_o) <= 1e-3
+
+
+@pytest.mark.parametrize("M", [1, 16, 64])
+def test_absmean_forward_decode_rows(orc, M):
+    """Few token rows: the decode GEMM multiplies absmean codes, whose range includes -8."""
+    wl = inputs.WORKLOADS["wdown_7b"]
+    note("absmean forward decode", M)
+    x = wl.activations(M)
+    W = inputs.make_weights(wl.N, wl.K)
+    T, alpha = orc.quantize_weights(W)
+    Wq, scale = B.quantize_weights(to_dev(W))
+    ws = B.forward_workspace(M, wl.K, 4)
+    y = to_host(B.forward(to_dev(x), Wq, scale, 4, True, norm=True, ws=ws, stat=B.HBL_STAT_ABSMEAN))
+    y_o, q_o, _, _ = orc.forward(x, T, alpha, 4, True, norm=True, stat=1, intermediates=True)
+    _codes_close(orc, to_host(ws[:M * wl.K // 2]).reshape(M, wl.K // 2), q_o, wl.K)
+    assert rel_fro(y, y_o) <= 1e-3
