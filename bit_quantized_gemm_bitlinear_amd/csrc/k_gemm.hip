@@ -13,10 +13,10 @@
 //   ternary:    word w of 16 2-bit fields -> (w << 6-2j) & 0xC0C0C0C0, j = 0..3, gives int8
 //               bytes equal to 64*t, in natural k order.
 //   INT8 codes: used as loaded.
-// Pairs of words are shifted as one 64-bit value (see fmma below).  When K is a multiple of
-// the stage depth the kernel is instantiated without the K-tail masks on its loads.
 // The int32 sum is therefore 1024*acc (INT4) or 64*acc (INT8); |acc| <= 127*K keeps it
-// below 2^31 for K <= 2^17 and the final arithmetic shift is exact.
+// below 2^31 for K <= 2^17 and the final arithmetic shift is exact.  Pairs of words are
+// shifted as one 64-bit value (see fmma below).  When K is a multiple of the stage depth
+// the kernel is instantiated without the K-tail masks on its loads.
 //
 // Tiling for large problems: a 512-thread block computes a 256 x 256 tile of y; its eight
 // waves (2 x 4) each own a 128 x 64 sub-tile of 32x32 MFMA tiles (128 int32 accumulators
