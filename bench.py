@@ -99,7 +99,7 @@ def act_bytes_per_token(K: int, abits: int, x_bytes: int) -> int:
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no multi-GPU path; "
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the library has no multi-GPU path; "
               "the layer shards over tokens with no exchange, so N GPUs would run this same kernel on M/N rows.",
               file=sys.stderr)
         sys.exit(2)
