@@ -72,22 +72,31 @@ def copy_calibration(mb: int) -> None:
     log(f"[bench] copied {mb} MiB three times")
 
 
+def code_digest(files) -> str:
+    """SHA-256 of kernel sources (names under the package's csrc/) with comments, trailing
+    blanks and empty lines removed, so that only a change of code invalidates a measurement."""
+    import hashlib
+    import re
+
+    h = hashlib.sha256()
+    for f in files:
+        text = open(os.path.join(ROOT, "bit_quantized_gemm_bitlinear_amd", "csrc", f)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        lines = (re.sub(r"//.*$", "", line).rstrip() for line in text.splitlines())
+        h.update("\n".join(line for line in lines if line).encode())
+    return h.hexdigest()
+
+
 def measured_traffic(kernel: str):
     """HBM-side bytes per launch of `kernel` from profiles/traffic.json (rocprofv3 FETCH_SIZE and
     WRITE_SIZE per dispatch, each scaled by what the counter reads for a copy of known size),
-    or None if the kernel's sources have changed since the counters were taken."""
-    import hashlib
-
+    or None if the kernel's code has changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     for e in json.load(open(path))["kernels"]:
-        if e["kernel"] != kernel:
-            continue
-        h = hashlib.sha256()
-        for f in e["sources"]:
-            h.update(open(os.path.join(ROOT, "bit_quantized_gemm_bitlinear_amd", "csrc", f), "rb").read())
-        return e["traffic_bytes"] if h.hexdigest() == e["sources_sha256"] else None
+        if e["kernel"] == kernel:
+            return e["traffic_bytes"] if code_digest(e["sources"]) == e.get("code_sha256") else None
     return None
 
 
