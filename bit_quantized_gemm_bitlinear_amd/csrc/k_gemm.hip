@@ -20,7 +20,8 @@
 //
 // Tiling for large problems: a 512-thread block computes a 256 x 256 tile of y; its eight
 // waves (2 x 4) each own a 128 x 64 sub-tile of 32x32 MFMA tiles (128 int32 accumulators
-// per lane, two waves per SIMD).  On gfx950 every VALU instruction issued beside an MFMA
+// per lane, two waves per SIMD).  The fused gate/up GEMM uses 128 x 256 tiles of four such
+// waves, two blocks per CU (see launch).  On gfx950 every VALU instruction issued beside an MFMA
 // costs issue time, so the 32x32x32 shape (twice the work per instruction of 16x16x64)
 // and a wide wave tile (each decoded fragment feeds 2-4 MFMAs) keep the decode overhead
 // low.  K advances in LDS stages (256 deep for INT4, 128 for INT8): the next stage is
@@ -73,7 +74,7 @@ struct Frag {
 // and the 16 k-values 16*(l/32) .. +15 of the 32-deep step; result row 8(v/4)+4(l/32)+v%4,
 // column l%32 in accumulator register v).  K advances in stages of BK (BK/32 k-steps).
 template <int ABITS, int BM, int BN, int WR, int WC, int BK, int MODE, bool FULLK>
-__global__ __launch_bounds__(64 * WR * WC) void k_gemm(const uint8_t* __restrict__ A, const float* __restrict__ deq,
+__global__ __launch_bounds__(64 * WR * WC) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm(const uint8_t* __restrict__ A, const float* __restrict__ deq,
                                                        const uint8_t* __restrict__ B,
                                                        const float* __restrict__ w_scale,
                                                        const float* __restrict__ w_scale_up, int M, int N, int K,
@@ -332,8 +333,15 @@ template <int ABITS, int MODE>
 hipError_t launch(const uint8_t* codes, const float* deq, const uint8_t* Wq, const float* w_scale,
                   const float* w_scale_up, int64_t M, int64_t K, int64_t N, int32_t* acc, void* out, hipStream_t s) {
   constexpr int BKBIG = ABITS == 4 ? 256 : 128;  // INT8 A tiles are twice as wide in LDS
-  if (use_big_tiles(M, N))
-    return launch_cfg<ABITS, 256, 256, 2, 4, BKBIG, MODE>(codes, deq, Wq, w_scale, w_scale_up, M, K, N, acc, out, s);
+  if (use_big_tiles(M, N)) {
+    // The fused SwiGLU epilogue is long (an exp and a division per output), so the gate/up
+    // GEMM runs 128 x 256 tiles with four waves: two blocks share a CU and one block's
+    // epilogue overlaps the other's MFMAs.
+    if constexpr (MODE >= 2)
+      return launch_cfg<ABITS, 128, 256, 1, 4, BKBIG, MODE>(codes, deq, Wq, w_scale, w_scale_up, M, K, N, acc, out, s);
+    else
+      return launch_cfg<ABITS, 256, 256, 2, 4, BKBIG, MODE>(codes, deq, Wq, w_scale, w_scale_up, M, K, N, acc, out, s);
+  }
   return launch_cfg<ABITS, 128, 128, 2, 2, 128, MODE>(codes, deq, Wq, w_scale, w_scale_up, M, K, N, acc, out, s);
 }
 
