@@ -322,14 +322,16 @@ def main():
         oracle.build()
         threads = oracle.num_threads()
         T, alpha = oracle.quantize_weights(W_np)
-        probe = 16
-        tp = time.perf_counter()
-        oracle.forward(x_np[:probe], T, alpha, abits, wl.use_hadamard, norm=wl.norm)
-        per_row = (time.perf_counter() - tp) / probe
-        rows = int(min(M, max(probe, args.cpu_seconds / max(per_row, 1e-9))))
-        tc = time.perf_counter()
-        oracle.forward(np.ascontiguousarray(x_np[:rows]), T, alpha, abits, wl.use_hadamard, norm=wl.norm)
-        dt = time.perf_counter() - tc
+        # Consecutive chunks of rows, each sized from the rate so far, until the target time
+        # is spent (or the rows run out); only the oracle calls are timed.
+        rows, dt, chunk = 0, 0.0, max(16, 2 * threads)
+        while rows < M and dt < args.cpu_seconds:
+            n = min(M - rows, chunk)
+            tc = time.perf_counter()
+            oracle.forward(np.ascontiguousarray(x_np[rows:rows + n]), T, alpha, abits, wl.use_hadamard, norm=wl.norm)
+            dt += time.perf_counter() - tc
+            rows += n
+            chunk = max(16, int(rows / dt * (args.cpu_seconds - dt)) + 1)
         cpu = {"value": rows / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
                "sample": f"first {rows} of {M} token rows of the same workload (weights ternarised beforehand, "
                          f"{dt:.1f} s of scalar C with OpenMP over rows)"}
