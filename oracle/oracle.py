@@ -20,7 +20,9 @@ BF16 = 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "hbl_oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# HBL_ORACLE_LIB names another build of hbl_oracle.c to load instead (the mutation tests
+# point it at copies with a planted mistake); build() then leaves it as it is.
+_LIB = os.environ.get("HBL_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lock = threading.Lock()
 _lib = None
 
@@ -29,12 +31,18 @@ def lib_path() -> str:
     return _LIB
 
 
+def compile_command(src: str, out: str) -> list:
+    return ["gcc", "-std=c11", "-O2", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-Wall",
+            "-Wextra", "-o", out, src, "-lm"]
+
+
 def build(force: bool = False) -> str:
     """Compile hbl_oracle.c with gcc (plain C11, OpenMP, no FMA contraction, no fast-math)."""
+    if os.environ.get("HBL_ORACLE_LIB"):
+        return _LIB
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + f".tmp{os.getpid()}"
-        cmd = ["gcc", "-std=c11", "-O2", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
-               "-fno-fast-math", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+        cmd = compile_command(_SRC, tmp)
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB)
     return _LIB

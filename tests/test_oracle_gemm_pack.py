@@ -45,6 +45,17 @@ def test_dequant_association(orc):
         assert y[0, j] == want
 
 
+def test_dequant_association_hand_case(orc):
+    """A case where the order of the two roundings shows (derived by hand; ulp(3) = 2^-22).
+    acc = 3, deq = alpha = 1 + 2^-23:
+      left to right: fl(3 deq) = 3 + 1.5 ulp -> tie, to even -> 3 + 2 ulp;
+                     fl((3 + 2 ulp) alpha) = 3 + 3.5 ulp + 2^-44 -> 3 + 4 ulp = 3 + 2^-20 (0x40400004)
+      scales first:  fl(deq alpha) = 1 + 2^-22;  3 (1 + 2^-22) = 3 + 3 ulp (0x40400003)"""
+    one_ulp = np.array([0x3F800001], np.uint32).view(np.float32)
+    y = orc.dequant(np.array([[3]], np.int32), one_ulp, float(one_ulp[0]))
+    assert y.view(np.uint32)[0, 0] == 0x40400004
+
+
 def test_swiglu_vs_scipy_expit(orc):
     rng = np.random.default_rng(1)
     g = (rng.standard_normal(10000) * 4).astype(np.float32)
