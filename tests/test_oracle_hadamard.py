@@ -78,3 +78,15 @@ def test_fwht_f32_deviation_from_fp64_is_small_at_16384(orc):
     z64 = orc.fwht_f64(x.astype(np.float64))
     scale = np.abs(z64).max(axis=1, keepdims=True)
     assert (np.abs(z32 - z64) / scale).max() < 14 * 2.0 ** -23
+
+
+def test_fwht_f32_stage_order_hand_case(orc):
+    """The fp32 transform runs its stages in ascending order (h = 1, 2, ...).  A 4-point case
+    where the order shows (derived by hand; 1 + 2^-24 is a tie that rounds to 1):
+      x = [1, 2^-24, 2^-24, 0]
+      h = 1: [fl(1 + 2^-24), 1 - 2^-24, 2^-24, 2^-24] = [1, 1 - 2^-24, 2^-24, 2^-24]
+      h = 2: [fl(1 + 2^-24), fl(1 - 2^-24 + 2^-24), 1 - 2^-24, 1 - 2^-23] = [1, 1, 1 - 2^-24, 1 - 2^-23]
+    (descending order gives [1, 1 - 2^-24, 1, 1 - 2^-23])."""
+    x = np.array([1.0, 2.0 ** -24, 2.0 ** -24, 0.0], np.float32)
+    z = orc.fwht_f32(x)
+    assert list(z.view(np.uint32)) == [0x3F800000, 0x3F800000, 0x3F7FFFFF, 0x3F7FFFFE]

@@ -24,6 +24,8 @@ MUTATIONS = [
     ("alpha: half the mean", "S += row_sum[n];", "S += row_sum[n] * 0.5;", 0),
     ("fwht f32: butterfly sign", "v[j + h] = a - b;", "v[j + h] = b - a;", 0),
     ("fwht f64: butterfly sign", "v[j + h] = a - b;", "v[j + h] = b - a;", 1),
+    ("fwht f32: stages in descending order", "for (int64_t h = 1; h < n; h *= 2)",
+     "for (int64_t h = n / 2; h >= 1; h /= 2)", 0),
     ("rms: sum of x instead of x^2", "ss += (double)xf * (double)xf;", "ss += (double)xf;", 0),
     ("absmean: sum of z instead of |z|", "sa += (double)fabsf(z[k]);", "sa += (double)z[k];", 0),
     ("absmean codes: ties away from zero", "float v = rintf(z[k] * s);", "float v = roundf(z[k] * s);", 0),
