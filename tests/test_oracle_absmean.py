@@ -62,3 +62,15 @@ def test_absmean_forward_composes(orc):
     np.testing.assert_array_equal(q, q2)
     np.testing.assert_array_equal(deq, d2)
     np.testing.assert_array_equal(acc, orc.gemm_s32(q, T))
+
+
+def test_absmean_scale_guard_row_below_threshold(orc):
+    """mean |z| below 2^-120: zero codes and deq = 0 (without the guard, 1/b = 2^121 is still a
+    finite fp32 here and the codes would be 4 and -4).  At the threshold the row is quantised."""
+    x = np.zeros((1, 8), np.float32)
+    x[0, 0], x[0, 1] = 2.0 ** -119, -(2.0 ** -119)     # mean |z| = 2^-118 / 8 = 2^-121
+    q, deq, _ = orc.quantize_activations(x, 4, False, stat=1)
+    assert not q.any() and deq[0] == 0.0
+    x[0, 0], x[0, 1] = 2.0 ** -118, -(2.0 ** -118)     # mean |z| = 2^-120: s = 2^120, codes 4 and -4
+    q, deq, _ = orc.quantize_activations(x, 4, False, stat=1)
+    assert q[0, 0] == 4 and q[0, 1] == -4 and deq[0] == np.float32(2.0 ** -120)

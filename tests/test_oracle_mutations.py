@@ -33,6 +33,9 @@ MUTATIONS = [
     ("absmean deq: 1/sqrt(K) dropped", "d = d * hK;", "d = d;", 0),
     ("absmax deq: 1/sqrt(K) dropped", "d = d * hK;", "d = d;", 1),
     ("deq: RMS factor dropped", "d = d * r;", "d = d;", 0),
+    ("absmean: scale guard only at zero", "if (b < 0x1p-120f) {", "if (b == 0.0f) {", 0),
+    ("absmax: scale guard only at zero", "if (g < 0x1p-120f) {", "if (g == 0.0f) {", 0),
+    ("qkv: scale guard only at zero", "const float s = g < 0x1p-120f ? 0.0f", "const float s = g == 0.0f ? 0.0f", 0),
     ("gemm: transposed weights", "s += (int32_t)q[m * K + k] * (int32_t)T[n * K + k];",
      "s += (int32_t)q[m * K + k] * (int32_t)T[k * N + n];", 0),
     ("dequant: scales multiplied first", "float v = (float)acc[m * N + n] * deq[m];\n      y[m * N + n] = v * alpha;",

@@ -78,3 +78,12 @@ def test_pack_bits_round_trip(orc, bits):
     # every code's bits sit where the format says
     flat = np.unpackbits(p, axis=1, bitorder="little").reshape(7, 64, bits)
     np.testing.assert_array_equal((flat * (1 << np.arange(bits))).sum(axis=2), u)
+
+
+def test_qkv_scale_guard_head_below_threshold(orc):
+    """A head with g < 2^-120 takes s = 0: every code is rint_ne(c) = rint_ne(3.5) = 4 at 3 bits
+    (without the guard, L / 2g is still finite here and the codes would span 0 .. 7)."""
+    h = np.zeros((1, 32), np.float32)
+    h[0, 0], h[0, 1] = 2.0 ** -121, -(2.0 ** -121)
+    u, g = orc.quantize_qkv(h, 3)
+    assert (u == 4).all() and g[0] == np.float32(2.0 ** -121)

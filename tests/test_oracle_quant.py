@@ -129,3 +129,17 @@ def test_fold_matches_textbook_order(orc):
         assert float((qt != q).mean()) <= 1e-4
         assert int(np.abs(qt.astype(np.int32) - q).max()) <= 1
         np.testing.assert_allclose(deqt, deq, rtol=1e-6)
+
+
+def test_scale_guard_row_below_threshold(orc):
+    """A row whose max |z| is below 2^-120 takes zero codes and deq = 0 (scale guard), although
+    Qb / max|z| would still be a finite fp32 here: without the guard this row would give codes
+    7 and -4 (2^-121 s = 7, -2^-122 s = -3.5, tie to even) for INT4."""
+    x = np.zeros((1, 64), np.float32)
+    x[0, 0], x[0, 5] = 2.0 ** -121, -(2.0 ** -122)
+    for abits in (4, 8):
+        q, deq, _ = orc.quantize_activations(x, abits, False)
+        assert not q.any() and deq[0] == 0.0
+    x[0, 0] = 2.0 ** -120          # at the threshold the row is quantised normally
+    q, deq, _ = orc.quantize_activations(x, 4, False)
+    assert q[0, 0] == 7 and q[0, 5] == -2 and deq[0] > 0       # -2^-122 * 7 * 2^120 = -1.75 -> -2
