@@ -510,9 +510,9 @@ def bench_decode(args, wl):
             if st != 0:
                 raise RuntimeError(L.hbl_last_error().decode())
 
-        def step(i):
+        def step(i, stream_handle=sh):
             ok(L.hbl_forward(x.data_ptr(), B.HBL_BF16, Wqs[i % copies].data_ptr(), scale.data_ptr(), M, K, N, 4, 1,
-                             B.HBL_NORM_RMS, None, 1e-5, y.data_ptr(), ws.data_ptr(), ws.numel(), sh))
+                             B.HBL_NORM_RMS, None, 1e-5, y.data_ptr(), ws.data_ptr(), ws.numel(), stream_handle))
 
         for i in range(max(args.warmup, copies)):
             step(i)
@@ -540,11 +540,32 @@ def bench_decode(args, wl):
         t_gemv = ev[1].elapsed_time(ev[2]) / steps * 1e-3
         gemv_bytes = N * K // 4 + M * K // 2 + 4 * M + 4 + 4 * M * N
         fused = bool(L.hbl_forward_fused(M, K, 4, 1))
+        # The same steps replayed from a HIP graph (one step per weight copy, captured once),
+        # as a serving loop would run them: no host launch cost between steps.
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            cs = torch.cuda.current_stream().cuda_stream
+            for i in range(copies):
+                step(i, cs)
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
+        reps = max(1, steps // copies)
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(reps):
+            graph.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        t_graph = g0.elapsed_time(g1) * 1e-3 / (reps * copies)
+        del graph
         per[M] = {"us_per_step": el * 1e6, "tokens_per_s": M / el,
+                  "graph_us_per_step": t_graph * 1e6, "graph_tokens_per_s": M / t_graph,
                   "path": "one fused kernel" if fused else "activation kernel + decode GEMM",
                   "separate_calls_us": {"actquant": t_act * 1e6, "gemv": t_gemv * 1e6},
                   "gemv_bytes": gemv_bytes, "gemv_gbs": gemv_bytes / t_gemv / 1e9}
-        log(f"[bench] decode M={M}: {el * 1e6:.2f} us/step ({per[M]['path']}); separate calls: act "
+        log(f"[bench] decode M={M}: {el * 1e6:.2f} us/step, {t_graph * 1e6:.2f} from a graph ({per[M]['path']}); "
+            f"separate calls: act "
             f"{t_act * 1e6:.2f} us, gemv {t_gemv * 1e6:.2f} us ({gemv_bytes / t_gemv / 1e9:.0f} GB/s)")
     head = per[wl.M]
     out = {"metric": "H-BitLinear a4 decode tokens/s, 7B-like Wdown (weights streamed from HBM)",
