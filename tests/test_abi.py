@@ -269,3 +269,25 @@ def test_stat_rejects(L):
     assert f(FAKE, 1, FAKE, FAKE, 4, 256, 8, 4, 1, 1, None, 1e-5, 3, FAKE, FAKE, 1 << 20, S) == B.HBL_ERR_INVALID_ARG
     assert f(FAKE, 1, FAKE, FAKE, 4, 256, 8, 8, 1, 1, None, 1e-5, 1, FAKE, FAKE, 1 << 20, S) == B.HBL_ERR_UNSUPPORTED
     assert f(FAKE, 1, FAKE, FAKE, 4, 256, 8, 4, 1, 1, None, 1e-5, 1, FAKE, FAKE, 10, S) == B.HBL_ERR_WORKSPACE
+
+
+def test_zero_rows_are_noops_everywhere(L):
+    """M = 0 (rows = 0, n = 0) is valid for every per-row call and returns HBL_OK without
+    touching the row buffers, which may then be null; the shape arguments are still checked."""
+    K, N, F = 256, 64, 64
+    assert L.hbl_gemm_dequant(None, None, FAKE, FAKE, 0, K, N, 4, None, S) == B.HBL_OK
+    assert L.hbl_quantize_activations_stat(None, B.HBL_BF16, 0, K, 0, None, 1e-5, 4, 1, B.HBL_STAT_ABSMEAN, None,
+                                           None, S) == B.HBL_OK
+    assert L.hbl_forward_stat(None, B.HBL_BF16, FAKE, FAKE, 0, K, N, 4, 1, 0, None, 1e-5, B.HBL_STAT_ABSMEAN, None,
+                              None, 0, S) == B.HBL_OK
+    assert L.hbl_swiglu(None, None, 0, None, S) == B.HBL_OK
+    assert L.hbl_gate_up_swiglu(None, None, FAKE, FAKE, FAKE, 0, K, F, 4, B.HBL_BF16, None, S) == B.HBL_OK
+    assert L.hbl_quantize_activations_fp6(None, B.HBL_BF16, 0, K, 0, None, 1e-5, 1, None, None, S) == B.HBL_OK
+    assert L.hbl_gemm_fp6fp4_s32(None, FAKE, 0, K, N, None, S) == B.HBL_OK
+    assert L.hbl_gemm_fp6fp4_dequant(None, None, FAKE, FAKE, 0, K, N, None, S) == B.HBL_OK
+    assert L.hbl_forward_fp6fp4(None, B.HBL_BF16, FAKE, FAKE, 0, K, N, 1, 0, None, 1e-5, None, None, 0, S) == B.HBL_OK
+    assert L.hbl_quantize_qkv(None, B.HBL_BF16, 0, 128, 3, None, None, S) == B.HBL_OK
+    assert L.hbl_dequantize_qkv(None, None, 0, 128, 3, None, S) == B.HBL_OK
+    # the shape is still validated when there are no rows
+    assert L.hbl_gemm_fp6fp4_s32(None, FAKE, 0, 100, N, None, S) == B.HBL_ERR_INVALID_ARG
+    assert L.hbl_quantize_qkv(None, B.HBL_BF16, 0, 128, 9, None, None, S) == B.HBL_ERR_INVALID_ARG
