@@ -117,3 +117,25 @@ def test_gemm_fp6fp4_max_k(orc, M):
     T[::3, ::7] = 0
     acc = to_host(B.gemm_fp6fp4_s32(to_dev(orc.pack_codes_fp6(q)), to_dev(orc.pack_weights_fp4(T)), K))
     np.testing.assert_array_equal(acc, orc.gemm_s32(q, T))
+
+
+@pytest.mark.parametrize("use_h,K", [(True, 4096), (False, 2112)])
+def test_forward_fp6fp4_fp32_gamma_matches_int4_path(orc, use_h, K):
+    """fp32 input with RMSNorm and a per-channel gamma, with and without the transform (the
+    plain path at a K that is no power of two): bit-identical to the INT4 path, and the
+    oracle's bar."""
+    M, N = 300, 200
+    note("forward fp6fp4 fp32 gamma", use_h, K)
+    x = inputs.bf16_bits_to_f32(inputs.make_activations("mixture", M, K, seed=K, outlier_frac=0.01,
+                                                        outlier_scale=40.0)) * np.float32(1.7)
+    gamma = np.random.default_rng(K + 1).uniform(0.5, 1.5, K).astype(np.float32)
+    W = inputs.make_weights(N, K, seed=3)
+    T, alpha = orc.quantize_weights(W)
+    Wq, scale = B.quantize_weights(to_dev(W))
+    Wq4 = B.weights_to_fp4(Wq, K)
+    xd, gd = to_dev(x), to_dev(gamma)
+    y6 = to_host(B.forward_fp6fp4(xd, Wq4, scale, use_h, norm=True, gamma=gd))
+    y4 = to_host(B.forward(xd, Wq, scale, 4, use_h, norm=True, gamma=gd))
+    np.testing.assert_array_equal(y6, y4)
+    y_o = orc.forward(x, T, alpha, 4, use_h, norm=True, gamma=gamma)
+    assert rel_fro(y6, y_o) <= 1e-3
