@@ -100,6 +100,42 @@ def measured_traffic(kernel: str):
     return None
 
 
+def mfma_ceiling():
+    """The int8 matrix-core rate this GPU sustains with no memory traffic and no other
+    instructions (libhbl_probe.so), in TOP/s, with operands shaped like the GEMM's widened
+    ones: bytes 16 q (q uniform in [-7, 7]) and 64 t (t in {-1, 0, 1}, 31 % zeros)."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    path = os.path.join(ROOT, "bit_quantized_gemm_bitlinear_amd", "libhbl_probe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    f = lib.hbl_probe_mfma_ceiling
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    rng = np.random.default_rng(7)
+    a = (rng.integers(-7, 8, 64 * 16) * 16).astype(np.int8)
+    t = rng.choice([-1, 0, 1], size=64 * 16, p=[0.345, 0.31, 0.345])
+    b = (t * 64).astype(np.int8)
+    ops = torch.from_numpy(np.concatenate([a, b]).view(np.uint8)).cuda()
+    blocks, iters = 768, 20000                  # one round of 4-wave blocks at 3 waves per SIMD
+    out = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
+    sh = torch.cuda.current_stream().cuda_stream
+    for _ in range(2):
+        if f(ops.data_ptr(), blocks, iters, out.data_ptr(), sh) != 0:
+            raise RuntimeError("hbl_probe_mfma_ceiling failed")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(3):
+        f(ops.data_ptr(), blocks, iters, out.data_ptr(), sh)
+    e1.record()
+    torch.cuda.synchronize()
+    t_one = e0.elapsed_time(e1) * 1e-3 / 3
+    return blocks * 4 * iters * 4 * 65536 / t_one / 1e12
+
+
 def act_bytes_per_token(K: int, abits: int, x_bytes: int) -> int:
     """Algorithmic HBM bytes of the activation kernel per token: read x, write codes + deq."""
     return K * x_bytes + K * abits // 8 + 4
@@ -314,6 +350,10 @@ def main():
     act_kernel = f"k_actquant_h<{K.bit_length() - 1}, {abits}, 1, 1>"
     act_roofline["traffic"] = measured_traffic(act_kernel) if wl.name == "wdown_7b" else None
 
+    ceiling = mfma_ceiling()
+    if ceiling:
+        log(f"[bench] MFMA-only int8 ceiling on this GPU: {ceiling:.0f} TOP/s; GEMM at {gemm_tops / ceiling:.1%} of it")
+
     # ---- CPU oracle baseline on a bounded sample of rows ----
     cpu = None
     if not args.no_cpu_baseline:
@@ -363,6 +403,10 @@ def main():
                      "kernel": "k_gemm (ternary x INT%d, v_mfma_i32_32x32x32_i8)" % abits,
                      "algorithmic": "2*M*N*K int8 ops per launch"},
         "roofline_actquant": act_roofline,
+        "mfma_ceiling": None if not ceiling else {
+            "tops": ceiling, "frac_of_peak": ceiling / PEAK_INT8_TOPS, "gemm_frac_of_ceiling": gemm_tops / ceiling,
+            "method": "v_mfma_i32_32x32x32_i8 only (no memory, no VALU), 4 independent chains per wave, 3 waves per "
+                      "SIMD, operands shaped like the GEMM's widened codes and weights"},
         "cpu_baseline": cpu,
         "alt_fp6fp4": alt,
         "alt_absmean": alt_mean,

@@ -21,6 +21,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libhbl.so")
+PROBE_SRC = os.path.join(PKG, "probe", "mfma_ceiling.hip")
+PROBE_LIB = os.path.join(PKG, "libhbl_probe.so")   # measurement aid for bench.py, not the layer
 ARCH = "gfx950"
 
 
@@ -69,6 +71,12 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
         if p.returncode != 0:
             raise RuntimeError("link failed:\n" + p.stderr)
         os.replace(tmp_lib, LIB)
+        tmp_probe = PROBE_LIB + f".tmp{os.getpid()}"
+        p = subprocess.run([hipcc(), "-x", "hip", "-shared", PROBE_SRC, "-o", tmp_probe] + common_flags(),
+                           capture_output=True, text=True)
+        if p.returncode != 0:
+            raise RuntimeError("probe build failed:\n" + p.stderr)
+        os.replace(tmp_probe, PROBE_LIB)
     finally:
         shutil.rmtree(tmpdir, ignore_errors=True)
     return LIB

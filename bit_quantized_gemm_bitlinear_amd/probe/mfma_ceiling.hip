@@ -1,0 +1,42 @@
+// mfma_ceiling.hip — a measurement aid, not part of the layer.  It measures the int8
+// matrix-core rate this GPU sustains with nothing else to do: no memory traffic, no VALU,
+// no LDS.  The GEMM's achieved rate is reported against it beside the published peak,
+// which assumes the peak clock; under MFMA load the clock sags.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+// Each wave runs `iters` rounds of four independent v_mfma_i32_32x32x32_i8 chains on operands
+// loaded from `ops` (2 x 64 lanes x 16 bytes; the operand bits matter, since the matrix
+// cores' power depends on them), then stores a checksum so the work is kept.
+__global__ __launch_bounds__(256) void k_mfma_ceiling(const v4i* __restrict__ ops, int iters, int* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const v4i a = ops[lane], b = ops[64 + lane];
+  v16i c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  for (int i = 0; i < iters; ++i) {
+    c0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(b, a, c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, a, c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_i32_32x32x32_i8(b, b, c3, 0, 0, 0);
+  }
+  int s = 0;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) s += c0[v] + c1[v] + c2[v] + c3[v];
+  out[blockIdx.x * 256 + threadIdx.x] = s;
+}
+
+}  // namespace
+
+// ops: device, 128 x 16 bytes; out: device, blocks * 256 ints.  Each launch performs
+// blocks * 4 waves * iters * 4 MFMAs of 32*32*32*2 = 65536 int8 ops.  Returns 0 on success.
+extern "C" int hbl_probe_mfma_ceiling(const void* ops, int blocks, int iters, int* out, void* stream) {
+  if (ops == nullptr || out == nullptr || blocks < 1 || iters < 1) return 1;
+  hipLaunchKernelGGL(k_mfma_ceiling, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
+                     static_cast<const v4i*>(ops), iters, out);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}

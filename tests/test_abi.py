@@ -291,3 +291,14 @@ def test_zero_rows_are_noops_everywhere(L):
     # the shape is still validated when there are no rows
     assert L.hbl_gemm_fp6fp4_s32(None, FAKE, 0, 100, N, None, S) == B.HBL_ERR_INVALID_ARG
     assert L.hbl_quantize_qkv(None, B.HBL_BF16, 0, 128, 9, None, None, S) == B.HBL_ERR_INVALID_ARG
+
+
+def test_probe_library_exports_its_entry_point():
+    """The measurement aid next to the library (the MFMA-only ceiling bench.py reports)."""
+    path = os.path.join(os.path.dirname(B.LIB_PATH), "libhbl_probe.so")
+    if not os.path.exists(path):
+        pytest.skip("libhbl_probe.so not built")
+    lib = ctypes.CDLL(path)
+    f = lib.hbl_probe_mfma_ceiling
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    assert f(None, 1, 1, FAKE, S) == 1 and f(FAKE, 0, 1, FAKE, S) == 1   # rejected before any HIP call
