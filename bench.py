@@ -100,10 +100,12 @@ def measured_traffic(kernel: str):
     return None
 
 
-def mfma_ceiling():
-    """The int8 matrix-core rate this GPU sustains with no memory traffic and no other
-    instructions (libhbl_probe.so), in TOP/s, with operands shaped like the GEMM's widened
-    ones: bytes 16 q (q uniform in [-7, 7]) and 64 t (t in {-1, 0, 1}, 31 % zeros)."""
+def mfma_ceiling(kind: str = "int8"):
+    """The matrix-core rate this GPU sustains with no memory traffic and no other
+    instructions (libhbl_probe.so), in TOP/s.  int8: v_mfma_i32_32x32x32_i8 with operands
+    shaped like the GEMM's widened ones, bytes 16 q (q uniform in [-7, 7]) and 64 t (t in
+    {-1, 0, 1}, 31 % zeros).  fp6fp4: v_mfma_scale_f32_32x32x64_f8f6f4 (FP6 x FP4) with
+    random encodings."""
     import ctypes
 
     import numpy as np
@@ -113,14 +115,19 @@ def mfma_ceiling():
     if not os.path.exists(path):
         return None
     lib = ctypes.CDLL(path)
-    f = lib.hbl_probe_mfma_ceiling
+    f = lib.hbl_probe_mfma_ceiling if kind == "int8" else lib.hbl_probe_mfma_f6f4_ceiling
     f.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     rng = np.random.default_rng(7)
-    a = (rng.integers(-7, 8, 64 * 16) * 16).astype(np.int8)
-    t = rng.choice([-1, 0, 1], size=64 * 16, p=[0.345, 0.31, 0.345])
-    b = (t * 64).astype(np.int8)
-    ops = torch.from_numpy(np.concatenate([a, b]).view(np.uint8)).cuda()
-    blocks, iters = 768, 20000                  # one round of 4-wave blocks at 3 waves per SIMD
+    if kind == "int8":
+        a = (rng.integers(-7, 8, 64 * 16) * 16).astype(np.int8)
+        t = rng.choice([-1, 0, 1], size=64 * 16, p=[0.345, 0.31, 0.345])
+        b = (t * 64).astype(np.int8)
+        ops = torch.from_numpy(np.concatenate([a, b]).view(np.uint8)).cuda()
+        per_mfma = 32 * 32 * 32 * 2
+    else:
+        ops = torch.from_numpy(rng.integers(0, 256, 128 * 32).astype(np.uint8)).cuda()
+        per_mfma = 32 * 32 * 64 * 2
+    blocks, iters = 768, 20000 if kind == "int8" else 10000  # one round of 4-wave blocks, 3 waves/SIMD
     out = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
     sh = torch.cuda.current_stream().cuda_stream
     for _ in range(2):
@@ -133,7 +140,7 @@ def mfma_ceiling():
     e1.record()
     torch.cuda.synchronize()
     t_one = e0.elapsed_time(e1) * 1e-3 / 3
-    return blocks * 4 * iters * 4 * 65536 / t_one / 1e12
+    return blocks * 4 * iters * 4 * per_mfma / t_one / 1e12
 
 
 def act_bytes_per_token(K: int, abits: int, x_bytes: int) -> int:
@@ -289,15 +296,20 @@ def main():
         tg6 = sum(e[1].elapsed_time(e[2]) for e in ev6) / n_ev * 1e-3
         same = bool(torch.equal(y6.view(torch.int32), y.view(torch.int32)))
         g6 = ops / tg6 / 1e12
+        ceil6 = mfma_ceiling("fp6fp4")
         alt = {"path": "FP6 (E2M3) INT4 codes x FP4 (E2M1) ternary weights, v_mfma_scale_f32_32x32x64_f8f6f4",
                "dtype": "fp6xfp4", "value": M * args.steps / el6, "unit": "tokens/s",
                "ms_per_step": el6 * 1e3 / args.steps, "outputs_bit_identical_to_int8_path": same,
                "kernels_us": {"actquant_fwht_fp6": ta6 * 1e6, "gemm_fp6fp4_dequant": tg6 * 1e6},
                "roofline": {"bound": "mfma", "achieved": g6, "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s",
                             "frac": g6 / PEAK_FP4_TFLOPS, "traffic": None, "kernel": "k_gemm_f6f4<256, 256, 4, 2, 1>",
-                            "algorithmic": "2*M*N*K ops per launch"}}
+                            "algorithmic": "2*M*N*K ops per launch"},
+               "mfma_ceiling": None if not ceil6 else {
+                   "tflops": ceil6, "frac_of_peak": ceil6 / PEAK_FP4_TFLOPS, "gemm_frac_of_ceiling": g6 / ceil6,
+                   "method": "v_mfma_scale_f32_32x32x64_f8f6f4 (FP6 x FP4) only, 4 independent chains per wave"}}
         log(f"[bench] fp6xfp4 path: {el6 * 1e3 / args.steps:.4f} ms/step, act {ta6 * 1e6:.1f} us, gemm "
-            f"{tg6 * 1e6:.1f} us ({g6:.0f} TFLOP/s), outputs identical: {same}")
+            f"{tg6 * 1e6:.1f} us ({g6:.0f} TFLOP/s), outputs identical: {same}"
+            + (f"; FP6 x FP4 MFMA-only ceiling {ceil6:.0f} TFLOP/s, GEMM at {g6 / ceil6:.1%} of it" if ceil6 else ""))
         del Wq4, ws6, y6
 
     # ---- the INT4 absmean statistic (the activation-statistic switch), reported beside ----

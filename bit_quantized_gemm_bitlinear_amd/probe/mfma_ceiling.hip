@@ -30,7 +30,40 @@ __global__ __launch_bounds__(256) void k_mfma_ceiling(const v4i* __restrict__ op
   out[blockIdx.x * 256 + threadIdx.x] = s;
 }
 
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// The same for v_mfma_scale_f32_32x32x64_f8f6f4 with A in FP6 E2M3 (6 registers used) and B
+// in FP4 E2M1 (4 registers used), block scales 2^0, as the FP6 x FP4 GEMM issues it.
+__global__ __launch_bounds__(256) void k_mfma_f6f4_ceiling(const v8i* __restrict__ ops, int iters,
+                                                           int* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  v8i a = ops[lane], b = ops[64 + lane];
+  a[6] = a[7] = 0;
+  b[4] = b[5] = b[6] = b[7] = 0;
+  v16f c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  for (int i = 0; i < iters; ++i) {
+    c0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c0, 2, 4, 0, 127, 0, 127);
+    c1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c1, 2, 4, 0, 127, 0, 127);
+    c2 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c2, 2, 4, 0, 127, 0, 127);
+    c3 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c3, 2, 4, 0, 127, 0, 127);
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) s += c0[v] + c1[v] + c2[v] + c3[v];
+  out[blockIdx.x * 256 + threadIdx.x] = (int)s;
+}
+
 }  // namespace
+
+// ops: device, 128 x 32 bytes (FP6 codes for A, FP4 weights for B); out: device, blocks * 256
+// ints.  Each launch performs blocks * 4 waves * iters * 4 MFMAs of 32*32*64*2 = 131072 ops.
+extern "C" int hbl_probe_mfma_f6f4_ceiling(const void* ops, int blocks, int iters, int* out, void* stream) {
+  if (ops == nullptr || out == nullptr || blocks < 1 || iters < 1) return 1;
+  hipLaunchKernelGGL(k_mfma_f6f4_ceiling, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
+                     static_cast<const v8i*>(ops), iters, out);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
 
 // ops: device, 128 x 16 bytes; out: device, blocks * 256 ints.  Each launch performs
 // blocks * 4 waves * iters * 4 MFMAs of 32*32*32*2 = 65536 int8 ops.  Returns 0 on success.
