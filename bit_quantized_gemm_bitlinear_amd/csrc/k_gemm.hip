@@ -24,10 +24,11 @@
 // waves, two blocks per CU (see launch).  On gfx950 every VALU instruction issued beside an MFMA
 // costs issue time, so the 32x32x32 shape (twice the work per instruction of 16x16x64)
 // and a wide wave tile (each decoded fragment feeds 2-4 MFMAs) keep the decode overhead
-// low.  K advances in LDS stages (256 deep for INT4, 128 for INT8): the next stage is
-// loaded from HBM into registers while the current one is multiplied out of LDS (double
-// buffered, one barrier per stage), and each 32-deep step's fragments are read from LDS
-// one step ahead.  LDS rows are padded so the fragment reads hit distinct banks.  Small
+// low.  K advances in LDS stages (256 deep for INT4, 128 for INT8), double buffered with
+// one barrier per stage.  Buffer loads fetch each stage two stages ahead into one of two
+// register sets, and the stage loaded during the previous one is stored to LDS in pieces
+// between the current stage's k-steps; each 32-deep step's fragments are read from LDS one
+// step ahead.  LDS rows are padded so the fragment reads hit distinct banks.  Small
 // problems use 128 x 128 tiles (4 waves) so that more CUs get work.
 //
 // Epilogues (MODE): 0 stores the int32 product, 1 the dequantised y.  2 and 3 are the fused
@@ -42,6 +43,8 @@
 
 namespace hbl {
 namespace {
+
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 // Block-to-tile order.  Blocks are dispatched round-robin over the 8 XCDs (block b runs on
 // XCD b % 8), and each XCD has its own L2.  The remap gives every XCD a contiguous chunk of
@@ -130,45 +133,73 @@ __global__ __launch_bounds__(64 * WR * WC) __attribute__((amdgpu_waves_per_eu(2)
     boff[i] = (uint32_t)(min(r, N - 1 - n0) * brow + 16 * c);
   }
 
-  uint4 ra[ALD], rb[BLD];
+  // Buffer resources over the tile's rows of A and B: the loads take the loop-invariant
+  // per-lane offsets above and the stage offset as a scalar.
+  const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(Ablk), (short)0, (int)(min(BM, M - m0) * arow), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(Bblk), (short)0, (int)(min(BN, N - n0) * brow), 0x00020000);
+  // Two register sets stage the global loads: set S receives stage kt + 2 while the other
+  // set, loaded a stage earlier, is stored to LDS.  S is a compile-time constant at every
+  // call; the sets are chosen with if constexpr and copied element by element, because a
+  // run-time subscript or pointer select on them makes the compiler keep them in memory.
+  struct Stage {
+    uint4 a[ALD], b[BLD];
+  };
+  Stage st0, st1;
+  auto stg = [&](auto S) __attribute__((always_inline)) -> Stage& {
+    if constexpr (decltype(S)::value == 0) return st0;
+    else return st1;
+  };
   // Load stage kt.  In the last stage only its first n64 64-deep slices exist; the rest of
   // the stage is zero-filled (zero weights and codes contribute nothing).
-  auto gload = [&](int kt, int n64) {
+  auto gload = [&](auto S, int kt, int n64) __attribute__((always_inline)) {
+    Stage& r = stg(S);
     const int va = n64 * 64 * ABITS / 8 / 16, vb = n64;
-    const uint8_t* ak = Ablk + (int64_t)kt * AB;
-    const uint8_t* bk = Bblk + (int64_t)kt * BB;
-#pragma unroll
-    for (int i = 0; i < ALD; ++i)
-      ra[i] = (int)((tid + NT * i) % ACH) < va ? *reinterpret_cast<const uint4*>(ak + aoff[i]) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < BLD; ++i)
-      rb[i] = (int)((tid + NT * i) % BCH) < vb ? *reinterpret_cast<const uint4*>(bk + boff[i]) : make_uint4(0, 0, 0, 0);
-  };
-  // FULLK (K a multiple of BK): every stage is whole, and the loads carry no masks.
-  auto load_stage = [&](int kt) {
-    if constexpr (FULLK) gload(kt, BK / 64);
-    else gload(kt, kt == KT - 1 ? last_k64 : BK / 64);
-  };
-  auto swrite = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < ALD; ++i) {
+      const v4u v = FULLK || (int)((tid + NT * i) % ACH) < va
+                        ? __builtin_amdgcn_raw_buffer_load_b128(rA, aoff[i], kt * AB, 0)
+                        : v4u{0, 0, 0, 0};
+      r.a[i] = make_uint4(v.x, v.y, v.z, v.w);
+    }
+#pragma unroll
+    for (int i = 0; i < BLD; ++i) {
+      const v4u v = FULLK || (int)((tid + NT * i) % BCH) < vb
+                        ? __builtin_amdgcn_raw_buffer_load_b128(rB, boff[i], kt * BB, 0)
+                        : v4u{0, 0, 0, 0};
+      r.b[i] = make_uint4(v.x, v.y, v.z, v.w);
+    }
+  };
+  // FULLK (K a multiple of BK): every stage is whole, and the loads carry no masks.
+  auto load_stage = [&](auto S, int kt) __attribute__((always_inline)) {
+    if constexpr (FULLK) gload(S, kt, BK / 64);
+    else gload(S, kt, kt == KT - 1 ? last_k64 : BK / 64);
+  };
+  // Store chunks [c0, c1) of register set S (A chunks first, then B chunks) into LDS buffer buf.
+  auto swrite = [&](auto S, int buf, int c0 = 0, int c1 = 1 << 20) __attribute__((always_inline)) {
+    const Stage& r = stg(S);
+#pragma unroll
+    for (int i = 0; i < ALD; ++i) {
+      if (i < c0 || i >= c1) continue;
       const int e = tid + NT * i;
       uint8_t* d = &sA[buf][(e / ACH) * AS + 16 * (e % ACH)];
       if constexpr (ABITS == 8) {
-        *reinterpret_cast<uint4*>(d) = ra[i];
+        *reinterpret_cast<uint4*>(d) = make_uint4(r.a[i].x, r.a[i].y, r.a[i].z, r.a[i].w);
       } else {
-        reinterpret_cast<uint2*>(d)[0] = make_uint2(ra[i].x, ra[i].y);
-        reinterpret_cast<uint2*>(d)[1] = make_uint2(ra[i].z, ra[i].w);
+        reinterpret_cast<uint2*>(d)[0] = make_uint2(r.a[i].x, r.a[i].y);
+        reinterpret_cast<uint2*>(d)[1] = make_uint2(r.a[i].z, r.a[i].w);
       }
     }
 #pragma unroll
     for (int i = 0; i < BLD; ++i) {
+      if (ALD + i < c0 || ALD + i >= c1) continue;
       const int e = tid + NT * i;
       uint32_t* d = reinterpret_cast<uint32_t*>(&sB[buf][(e / BCH) * BS + 16 * (e % BCH)]);
-      d[0] = rb[i].x;
-      d[1] = rb[i].y;
-      d[2] = rb[i].z;
-      d[3] = rb[i].w;
+      d[0] = r.b[i].x;
+      d[1] = r.b[i].y;
+      d[2] = r.b[i].z;
+      d[3] = r.b[i].w;
     }
   };
 
@@ -235,27 +266,44 @@ __global__ __launch_bounds__(64 * WR * WC) __attribute__((amdgpu_waves_per_eu(2)
     }
   };
 
+  // Software pipeline over two LDS buffers and two register sets: the loads of stage kt + 2
+  // are issued at the start of stage kt, and stage kt + 1 (loaded during stage kt - 1) is
+  // stored into the other LDS buffer a few chunks after each pair of k-steps of kt, so a
+  // load has about a stage to arrive and the LDS stores are spread between the MFMAs.
+  // Within a stage the k-steps ping-pong between two fragment sets, each read from LDS one
+  // step ahead.  Loads and stores are unconditional (past the last stage they reload it and
+  // store into the idle buffer), so the compiler's memory-counter waits stay exact: a
+  // branch around them would make it wait for the loads just issued as well.
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
   F f0, f1;
-  load_stage(0);
-  swrite(0);
-  __syncthreads();
-  fread(0, 0, f0);
-  for (int kt = 0; kt < KT; ++kt) {
+  auto stage = [&](auto S, int kt) __attribute__((always_inline)) {
+    constexpr int set = decltype(S)::value;
     const int buf = kt & 1;
-    const bool has_next = kt + 1 < KT;
-    if (has_next) load_stage(kt + 1);
-    // k-steps ping-pong between two fragment sets, each read one step ahead.
+    load_stage(S, min(kt + 2, KT - 1));
+    constexpr int NCH = ALD + BLD, PER = (NCH + KS / 2 - 1) / (KS / 2);
 #pragma unroll
     for (int ks = 0; ks < KS; ks += 2) {
       fread(buf, ks + 1, f1);
       fmma(f0);
       if (ks + 2 < KS) fread(buf, ks + 2, f0);
+      swrite(std::integral_constant<int, 1 - set>{}, buf ^ 1, (ks / 2) * PER, (ks / 2 + 1) * PER);
       fmma(f1);
     }
-    if (has_next) swrite(buf ^ 1);
     __syncthreads();
-    if (has_next) fread(buf ^ 1, 0, f0);
+    fread(buf ^ 1, 0, f0);
+  };
+  load_stage(I0{}, 0);
+  load_stage(I1{}, min(1, KT - 1));
+  swrite(I0{}, 0);
+  __syncthreads();
+  fread(0, 0, f0);
+  int kt = 0;
+  for (; kt + 1 < KT; kt += 2) {
+    stage(I0{}, kt);
+    stage(I1{}, kt + 1);
   }
+  if (kt < KT) stage(I0{}, kt);
 
   if constexpr (MODE >= 2) {
     // Fused gate/up: B rows n0 + 64*wn + [0, 32) are gate rows and [32, 64) the up rows of
