@@ -218,11 +218,18 @@ __global__ __launch_bounds__(64 * WR * WC) __attribute__((amdgpu_waves_per_eu(2)
     for (int j = 0; j < TN; ++j) f.b[j] = *reinterpret_cast<const uint32_t*>(&sB[buf][brow0 + 32 * j * BS + ks * 8]);
   };
 
+  // The accumulators live in the AGPR file: the empty asm with an "a" constraint makes the
+  // compiler select the AGPR form of the MFMAs, so the matrix core reads and writes them
+  // outside the VGPRs the widening and address arithmetic use (about 3 % faster than VGPR
+  // accumulators at the same occupancy; 128 AGPRs + at most 128 VGPRs per lane).
   v16i acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = v16i{};
+    for (int j = 0; j < TN; ++j) {
+      acc[i][j] = v16i{};
+      asm volatile("" : "+a"(acc[i][j]));
+    }
 
   // Widening with 64-bit shifts: one v_lshlrev_b64 shifts two words, and the byte masks clear
   // the bits that cross from the low word into the high one (they land below the kept bits

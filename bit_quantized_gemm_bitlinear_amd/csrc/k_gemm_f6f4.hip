@@ -182,11 +182,16 @@ __global__ __launch_bounds__(64 * WR * WC) void k_gemm_f6f4(const uint8_t* __res
     for (int j = 0; j < TN; ++j) f.b[j] = *reinterpret_cast<const uint4*>(&sB[buf][brow0 + 32 * j * BS + ks * 32]);
   };
 
+  // Accumulators in the AGPR file (the "a" constraint selects the AGPR form of the MFMAs),
+  // away from the VGPRs the loads and fragments use.
   v16f acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = v16f{};
+    for (int j = 0; j < TN; ++j) {
+      acc[i][j] = v16f{};
+      asm volatile("" : "+a"(acc[i][j]));
+    }
 
   auto fmma = [&](const Frag& f) {
 #pragma unroll
