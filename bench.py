@@ -302,7 +302,9 @@ def main():
                "ms_per_step": el6 * 1e3 / args.steps, "outputs_bit_identical_to_int8_path": same,
                "kernels_us": {"actquant_fwht_fp6": ta6 * 1e6, "gemm_fp6fp4_dequant": tg6 * 1e6},
                "roofline": {"bound": "mfma", "achieved": g6, "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s",
-                            "frac": g6 / PEAK_FP4_TFLOPS, "traffic": None, "kernel": "k_gemm_f6f4<256, 256, 4, 2, 1>",
+                            "frac": g6 / PEAK_FP4_TFLOPS,
+                            "traffic": measured_traffic("k_gemm_f6f4<256, 256, 4, 2, 1, true>"),
+                            "kernel": "k_gemm_f6f4<256, 256, 4, 2, 1, true>",
                             "algorithmic": "2*M*N*K ops per launch"},
                "mfma_ceiling": None if not ceil6 else {
                    "tflops": ceil6, "frac_of_peak": ceil6 / PEAK_FP4_TFLOPS, "gemm_frac_of_ceiling": g6 / ceil6,

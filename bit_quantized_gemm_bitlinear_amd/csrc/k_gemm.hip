@@ -312,17 +312,20 @@ __global__ __launch_bounds__(64 * WR * WC) __attribute__((amdgpu_waves_per_eu(2)
   }
   if (kt < KT) stage(I0{}, kt);
 
+  // The epilogue takes the lane index afresh (v_mbcnt) rather than keeping the main loop's
+  // lane-derived values live across it, which at 128 VGPRs made the compiler spill them.
+  const int el = __lane_id();
   if constexpr (MODE >= 2) {
     // Fused gate/up: B rows n0 + 64*wn + [0, 32) are gate rows and [32, 64) the up rows of
     // the same 32 outputs h[:, n0/2 + 32*wn + (lane % 32)]; N here counts both (2F rows).
     const float ag = w_scale[0], au = w_scale_up[0];
     const int F = N / 2;
-    const int n = n0 / 2 + wn * 32 + (lane & 31);
+    const int n = n0 / 2 + wn * 32 + (el & 31);
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int m = m0 + wm * WM + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        const int m = m0 + wm * WM + 32 * i + 8 * (v >> 2) + 4 * (el >> 5) + (v & 3);
         if (m >= M || n >= F) continue;
         const float dm = deq[m];
         const float g = __fmul_rn(__fmul_rn((float)(acc[i][0][v] >> SHIFT), dm), ag);
@@ -340,13 +343,13 @@ __global__ __launch_bounds__(64 * WR * WC) __attribute__((amdgpu_waves_per_eu(2)
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int m = m0 + wm * WM + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      const int m = m0 + wm * WM + 32 * i + 8 * (v >> 2) + 4 * (el >> 5) + (v & 3);
       if (m >= M) continue;
       float dm = 0.0f;
       if constexpr (MODE == 1) dm = deq[m];
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const int n = n0 + wn * WN + 32 * j + (lane & 31);
+        const int n = n0 + wn * WN + 32 * j + (el & 31);
         if (n >= N) continue;
         const int val = acc[i][j][v] >> SHIFT;
         if constexpr (MODE == 0) {

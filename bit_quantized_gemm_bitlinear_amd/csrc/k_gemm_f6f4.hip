@@ -256,19 +256,22 @@ __global__ __launch_bounds__(64 * WR * WC) void k_gemm_f6f4(const uint8_t* __res
   }
   if (kt < KT) stage(I0{}, kt);
 
+  // The epilogue takes the lane index afresh (v_mbcnt) rather than keeping the main loop's
+  // lane-derived values live across it, which at 128 VGPRs made the compiler spill them.
+  const int el = __lane_id();
   float alpha = 0.0f;
   if constexpr (MODE == 1) alpha = w_scale[0];
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int m = m0 + wm * WM + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      const int m = m0 + wm * WM + 32 * i + 8 * (v >> 2) + 4 * (el >> 5) + (v & 3);
       if (m >= M) continue;
       float dm = 0.0f;
       if constexpr (MODE == 1) dm = deq[m];
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const int n = n0 + wn * WN + 32 * j + (lane & 31);
+        const int n = n0 + wn * WN + 32 * j + (el & 31);
         if (n >= N) continue;
         const float a = acc[i][j][v];  // an exact integer
         if constexpr (MODE == 0) {
