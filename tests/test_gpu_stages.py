@@ -115,10 +115,13 @@ def test_actquant_plain_bitlinear(orc, K, abits):
     _act_case(orc, x, abits, False, norm=False)
 
 
-# Tile configurations: 128 x 128 tiles for the small problems, 256 x 256 for (2500, *, 2200);
-# K = 320 and 576 leave a partial last stage (masked loads), the other K fill every stage.
+# Tile configurations: 128 x 128 tiles for the small problems, 256 x 256 for (2500, *, 2200) and
+# (2100, *, 2060); K = 64, 320, 384 and 576 leave a partial last stage (masked loads), the other
+# K fill every stage.  The 256 x 256 cases run 1 to 8 stages (INT4: 256 deep, INT8: 128 deep),
+# odd and even counts, so the two-stage-ahead load pipeline is exercised at its start and end.
 @pytest.mark.parametrize("M,K,N", [(1, 64, 1), (16, 256, 256), (200, 320, 136), (129, 1024, 257), (300, 2048, 520),
-                                   (64, 16384, 64), (2500, 576, 2200), (2500, 1024, 2200)])
+                                   (64, 16384, 64), (2500, 576, 2200), (2500, 1024, 2200), (2100, 64, 2060),
+                                   (2100, 256, 2060), (2100, 384, 2060), (2100, 768, 2060)])
 @pytest.mark.parametrize("abits", [4, 8])
 def test_gemm_s32_bit_exact(orc, M, K, N, abits):
     note("gemm_s32", M, K, N, abits)
