@@ -19,10 +19,25 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
 }
 
-// SwiGLU gate: silu(g) * u with silu(v) = v / (1 + exp(-v)), in fp32 with the device expf.
-// Shared by the standalone kernel and the fused GEMM epilogue so both give the same bits.
+// e^x for the SwiGLU gate, in a few instructions: x log2(e) = n + r with n an integer and
+// |r| <= 1/2, where log2(e) is split into its fp32 value and the remainder so that r carries
+// only its own rounding; 2^r comes from v_exp_f32 and n is added to the exponent
+// (v_ldexp_f32, which gives 0 or inf past the fp32 range).  x is clamped to +-150 first, far
+// outside that range, so that the reduction never sees an infinity.
+__device__ __forceinline__ float exp_gate(float x) {
+  const float l2e_hi = 1.44269502162933349609375f;  // fp32 nearest to log2(e)
+  const float l2e_lo = 1.9259629911e-8f;            // log2(e) - l2e_hi
+  x = __builtin_fminf(__builtin_fmaxf(x, -150.0f), 150.0f);
+  const float n = __builtin_rintf(x * l2e_hi);
+  const float r = __builtin_fmaf(x, l2e_hi, -n) + x * l2e_lo;
+  return __builtin_amdgcn_ldexpf(__builtin_amdgcn_exp2f(r), (int)n);
+}
+
+// SwiGLU gate: silu(g) * u with silu(v) = v / (1 + exp(-v)) = v * rcp(1 + exp(-v)), in fp32
+// with exp_gate and v_rcp_f32 (each about an ulp).  Shared by the standalone kernel and the
+// fused GEMM epilogue so both give the same bits.
 __device__ __forceinline__ float silu_mul(float g, float u) {
-  const float sg = g / (1.0f + expf(-g));
+  const float sg = g * __builtin_amdgcn_rcpf(1.0f + exp_gate(-g));
   return sg * u;
 }
 

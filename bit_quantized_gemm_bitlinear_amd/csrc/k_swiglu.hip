@@ -3,7 +3,8 @@
 // BitNet v2 write-up, section "BitNet v2：原生4位激活": the model is built from LLaMA-like
 // parts (RMS normalisation, SwishGLU, no biases); the FFN's down projection Wdown is the
 // H-BitLinear that consumes h.  silu(v) = v / (1 + exp(-v)), evaluated in fp32 with the
-// device expf (a few ulp from the correctly rounded value).
+// exponential and reciprocal instructions (silu_mul; a few ulp from the correctly rounded
+// value).
 #include "hbl_device.h"
 #include "hbl_internal.h"
 

@@ -171,6 +171,23 @@ def test_swiglu(orc):
     assert_close_ulps(h, orc.swiglu(g, u), 4, "swiglu")
 
 
+def test_swiglu_range(orc):
+    """silu(g) * u over the whole range where fp32 e^-g is finite and 1 / (1 + e^-g) is normal:
+    g in [-87, 88] densely, with u = 1 (the gate alone) and random u.  Below g = -87.3 the true
+    |h| is under 1e-35 and the fp32 gate gives a value that small or zero."""
+    note("swiglu range")
+    g = np.concatenate([np.linspace(-87.0, 88.0, 400001), [0.0, 1e-30, -1e-30, 1e-6, -1e-6]]).astype(np.float32)
+    for u in (np.ones_like(g), np.random.default_rng(9).standard_normal(g.size).astype(np.float32)):
+        h = to_host(B.swiglu(to_dev(g), to_dev(u)))
+        want = orc.swiglu(g, u)
+        err = np.abs(h.astype(np.float64) - want) / np.maximum(np.abs(want.astype(np.float64)), 1e-30)
+        note("swiglu range: max relative error", float(err.max()), "= ulp", float(err.max() / 2.0 ** -23))
+        assert_close_ulps(h, want, 4, "swiglu range")
+    gn = np.linspace(-100.0, -87.5, 1001).astype(np.float32)
+    h = to_host(B.swiglu(to_dev(gn), to_dev(np.ones_like(gn))))
+    assert np.all(np.abs(h) <= 1e-35) and np.all(np.abs(orc.swiglu(gn, np.ones_like(gn))) <= 1e-35)
+
+
 @pytest.mark.parametrize("M", [16, 65])
 @pytest.mark.parametrize("abits", [4, 8])
 def test_gemm_s32_max_k(orc, M, abits):
