@@ -7,8 +7,9 @@
 // int8 matrix cores (v_mfma_i32_16x16x64_i8), whose rate keeps the arithmetic well below the
 // load time up to M = 64.
 //
-// Block b owns 16 output columns (weight rows n0 .. n0+15) and all M tokens; its 8 waves
-// split K and their int32 tiles are summed in LDS.  The integer sum is exact, so the result
+// Block b owns 16 output columns (weight rows n0 .. n0+15) and all M tokens; its waves (8 for
+// M <= 16, 16 above, where each lane also loads the codes of up to four token tiles) split K
+// and their int32 tiles are summed in LDS.  The integer sum is exact, so the result
 // equals the large-M kernel bit for bit.
 //
 // K order inside a 256-deep group C: lane (g, r) = (lane / 16, lane % 16) loads the 16-byte
@@ -20,8 +21,6 @@
 
 namespace hbl {
 namespace {
-
-constexpr int GV_WAVES = 8;
 
 template <int ABITS>
 struct AChunk;  // one lane's 64 codes of a 64-deep chunk
@@ -54,8 +53,8 @@ __device__ __forceinline__ v4i b_operand(uint32_t w) {
              (int)(w & 0xC0C0C0C0u)};
 }
 
-// MT: 16-row token tiles (M <= 16 MT); U: 256-deep groups loaded per batch.
-template <int ABITS, int MT, int U, int MODE>
+// MT: 16-row token tiles (M <= 16 MT); U: 256-deep groups loaded per batch; GV_WAVES waves.
+template <int ABITS, int MT, int U, int GV_WAVES, int MODE>
 __global__ __launch_bounds__(64 * GV_WAVES) void k_gemv(const uint8_t* __restrict__ A, const float* __restrict__ deq,
                                                         const uint8_t* __restrict__ B,
                                                         const float* __restrict__ w_scale, int M, int N, int K,
@@ -140,17 +139,17 @@ __global__ __launch_bounds__(64 * GV_WAVES) void k_gemv(const uint8_t* __restric
 template <int ABITS, int MODE>
 hipError_t launch_mode(const uint8_t* codes, const float* deq, const uint8_t* Wq, const float* w_scale, int64_t M,
                        int64_t K, int64_t N, int32_t* acc, float* y, hipStream_t s) {
-  const dim3 grid((unsigned)((N + 15) / 16)), block(64 * GV_WAVES);
+  const dim3 grid((unsigned)((N + 15) / 16));
   const int mt = (int)((M + 15) / 16);
   if (mt == 1)
-    hipLaunchKernelGGL((k_gemv<ABITS, 1, 4, MODE>), grid, block, 0, s, codes, deq, Wq, w_scale, (int)M, (int)N,
-                       (int)K, acc, y);
+    hipLaunchKernelGGL((k_gemv<ABITS, 1, 4, 8, MODE>), grid, dim3(64 * 8), 0, s, codes, deq, Wq, w_scale, (int)M,
+                       (int)N, (int)K, acc, y);
   else if (mt == 2)
-    hipLaunchKernelGGL((k_gemv<ABITS, 2, 4, MODE>), grid, block, 0, s, codes, deq, Wq, w_scale, (int)M, (int)N,
-                       (int)K, acc, y);
+    hipLaunchKernelGGL((k_gemv<ABITS, 2, 4, 16, MODE>), grid, dim3(64 * 16), 0, s, codes, deq, Wq, w_scale, (int)M,
+                       (int)N, (int)K, acc, y);
   else
-    hipLaunchKernelGGL((k_gemv<ABITS, 4, 2, MODE>), grid, block, 0, s, codes, deq, Wq, w_scale, (int)M, (int)N,
-                       (int)K, acc, y);
+    hipLaunchKernelGGL((k_gemv<ABITS, 4, 2, 16, MODE>), grid, dim3(64 * 16), 0, s, codes, deq, Wq, w_scale, (int)M,
+                       (int)N, (int)K, acc, y);
   return hipGetLastError();
 }
 
