@@ -360,7 +360,7 @@ def main():
     else:
         act_roofline = {"bound": "hbm", **act_hbm}
     act_roofline["traffic_unit"] = "HBM-side bytes per launch (FETCH_SIZE x2.0 + WRITE_SIZE x1.0)"
-    gemm_kernel = f"k_gemm<{abits}, 256, 256, 2, 4, {256 if abits == 4 else 128}, 1, {'true' if K % (256 if abits == 4 else 128) == 0 else 'false'}>"
+    gemm_kernel = f"k_gemm<{abits}, 256, 256, 2, 4, {256 if abits == 4 else 128}, 1, {'true' if K % (256 if abits == 4 else 128) == 0 else 'false'}, false>"
     act_kernel = f"k_actquant_h<{K.bit_length() - 1}, {abits}, 1, 1>"
     act_roofline["traffic"] = measured_traffic(act_kernel) if wl.name == "wdown_7b" else None
 
@@ -524,7 +524,7 @@ def bench_ffn(args, wl):
            "parts_us": {name: v for (name, _), v in zip(parts, sums)},
            "roofline": {"bound": "mfma", "achieved": gu_tops, "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
                         "frac": gu_tops / PEAK_INT8_TOPS,
-                        "traffic": measured_traffic("k_gemm<4, 128, 256, 1, 4, 256, 3, true>"),
+                        "traffic": measured_traffic("k_gemm<4, 128, 256, 1, 4, 256, 3, true, false>"),
                         "traffic_unit": "HBM-side bytes per launch (FETCH_SIZE x2.0 + WRITE_SIZE x1.0)",
                         "kernel": "k_gemm fused gate/up + SwiGLU epilogue (v_mfma_i32_32x32x32_i8)",
                         "algorithmic": "2*M*(2*ffn)*hidden int8 ops per launch"}}

@@ -36,6 +36,7 @@
 // of 32 rows, so the two 32-column MFMA tiles of a wave hold g and u for the same outputs in
 // the same lanes; the epilogue dequantises both with their own weight scales and stores
 // h = silu(g) * u once (fp32 for 2, bf16 for 3) instead of writing g and u.
+#include <algorithm>
 #include <type_traits>
 
 #include "hbl_device.h"
@@ -76,12 +77,17 @@ struct Frag {
 // (BM/WR) x (BN/WC) as 32x32 tiles of v_mfma_i32_32x32x32_i8 (lane l holds row/column l%32
 // and the 16 k-values 16*(l/32) .. +15 of the 32-deep step; result row 8(v/4)+4(l/32)+v%4,
 // column l%32 in accumulator register v).  K advances in stages of BK (BK/32 k-steps).
-template <int ABITS, int BM, int BN, int WR, int WC, int BK, int MODE, bool FULLK>
+//
+// SPLIT: the block multiplies only the stages [blockIdx.y * kt_per, + kt_per) of K and adds
+// its int32 result into acc_out with atomics (exact: integer sums do not depend on order);
+// the caller zeroes acc_out before and, for MODE 1, dequantises it after.
+template <int ABITS, int BM, int BN, int WR, int WC, int BK, int MODE, bool FULLK, bool SPLIT>
 __global__ __launch_bounds__(64 * WR * WC) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm(const uint8_t* __restrict__ A, const float* __restrict__ deq,
                                                        const uint8_t* __restrict__ B,
                                                        const float* __restrict__ w_scale,
                                                        const float* __restrict__ w_scale_up, int M, int N, int K,
-                                                       int32_t* __restrict__ acc_out, void* __restrict__ out) {
+                                                       int32_t* __restrict__ acc_out, void* __restrict__ out,
+                                                       int kt_per) {
   constexpr int NT = 64 * WR * WC;                  // threads per block
   constexpr int KS = BK / 32;                       // k-steps per stage
   constexpr int AB = BK * ABITS / 8;                // bytes of one A row per stage
@@ -98,6 +104,7 @@ __global__ __launch_bounds__(64 * WR * WC) __attribute__((amdgpu_waves_per_eu(2)
   static_assert(KS % 2 == 0, "stages hold an even number of k-steps");
   static_assert(ALD >= 1 && BLD >= 1 && ALD * NT == BM * ACH && BLD * NT == BN * BCH, "tile/thread mismatch");
   static_assert(MODE < 2 || WN == 64, "the fused gate/up epilogue pairs a wave's two 32-column tiles");
+  static_assert(!SPLIT || MODE < 2, "split K is for the int32 and dequant epilogues");
 
   __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * AS];
   __shared__ __attribute__((aligned(16))) uint8_t sB[2][BN * BS];
@@ -114,6 +121,8 @@ __global__ __launch_bounds__(64 * WR * WC) __attribute__((amdgpu_waves_per_eu(2)
   const int64_t brow = K / 4;
   const int KT = (K + BK - 1) / BK;
   const int last_k64 = (K - (KT - 1) * BK) / 64;   // 64-deep slices in the last stage
+  const int kb = SPLIT ? (int)blockIdx.y * kt_per : 0;   // this block's first stage
+  const int KTL = SPLIT ? min(KT - kb, kt_per) : KT;     // and its number of stages
 
   // Per-thread global sources, 32-bit offsets from the tile's first row.  Rows past M
   // (columns past N) are clamped to the last valid one: their products land in accumulator
@@ -284,10 +293,10 @@ __global__ __launch_bounds__(64 * WR * WC) __attribute__((amdgpu_waves_per_eu(2)
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   F f0, f1;
-  auto stage = [&](auto S, int kt) __attribute__((always_inline)) {
+  auto stage = [&](auto S, int kt) __attribute__((always_inline)) {  // kt counts this block's stages
     constexpr int set = decltype(S)::value;
     const int buf = kt & 1;
-    load_stage(S, min(kt + 2, KT - 1));
+    load_stage(S, kb + min(kt + 2, KTL - 1));
     constexpr int NCH = ALD + BLD, PER = (NCH + KS / 2 - 1) / (KS / 2);
 #pragma unroll
     for (int ks = 0; ks < KS; ks += 2) {
@@ -300,17 +309,17 @@ __global__ __launch_bounds__(64 * WR * WC) __attribute__((amdgpu_waves_per_eu(2)
     __syncthreads();
     fread(buf ^ 1, 0, f0);
   };
-  load_stage(I0{}, 0);
-  load_stage(I1{}, min(1, KT - 1));
+  load_stage(I0{}, kb);
+  load_stage(I1{}, kb + min(1, KTL - 1));
   swrite(I0{}, 0);
   __syncthreads();
   fread(0, 0, f0);
   int kt = 0;
-  for (; kt + 1 < KT; kt += 2) {
+  for (; kt + 1 < KTL; kt += 2) {
     stage(I0{}, kt);
     stage(I1{}, kt + 1);
   }
-  if (kt < KT) stage(I0{}, kt);
+  if (kt < KTL) stage(I0{}, kt);
 
   // The epilogue takes the lane index afresh (v_mbcnt) rather than keeping the main loop's
   // lane-derived values live across it, which at 128 VGPRs made the compiler spill them.
@@ -352,7 +361,9 @@ __global__ __launch_bounds__(64 * WR * WC) __attribute__((amdgpu_waves_per_eu(2)
         const int n = n0 + wn * WN + 32 * j + (el & 31);
         if (n >= N) continue;
         const int val = acc[i][j][v] >> SHIFT;
-        if constexpr (MODE == 0) {
+        if constexpr (SPLIT) {
+          atomicAdd(&acc_out[(int64_t)m * N + n], val);
+        } else if constexpr (MODE == 0) {
           acc_out[(int64_t)m * N + n] = val;
         } else {
           static_cast<float*>(out)[(int64_t)m * N + n] = __fmul_rn(__fmul_rn((float)val, dm), alpha);
@@ -362,24 +373,63 @@ __global__ __launch_bounds__(64 * WR * WC) __attribute__((amdgpu_waves_per_eu(2)
   }
 }
 
+// Zero n int32 (split-K accumulators; a kernel rather than a memset so that the sequence can
+// be captured in a graph).
+__global__ __launch_bounds__(256) void k_zero32(int32_t* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0;
+}
+
+// In place: the int32 product acc[m, n] -> y[m, n] = fl(fl((float)acc * deq[m]) * alpha).
+__global__ __launch_bounds__(256) void k_dequant32(void* __restrict__ buf, const float* __restrict__ deq,
+                                                   const float* __restrict__ w_scale, int64_t M, int64_t N) {
+  const float alpha = w_scale[0];
+  int32_t* acc = static_cast<int32_t*>(buf);
+  float* y = static_cast<float*>(buf);
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < M * N; i += (int64_t)gridDim.x * 256)
+    y[i] = __fmul_rn(__fmul_rn((float)acc[i], deq[i / N]), alpha);
+}
+
 template <int ABITS, int BM, int BN, int WR, int WC, int BK, int MODE>
 hipError_t launch_cfg(const uint8_t* codes, const float* deq, const uint8_t* Wq, const float* w_scale,
                       const float* w_scale_up, int64_t M, int64_t K, int64_t N, int32_t* acc, void* out,
-                      hipStream_t s) {
+                      int splits, hipStream_t s) {
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const int KT = (int)((K + BK - 1) / BK);
+  if constexpr (MODE <= 1) {
+    if (splits > 1) {
+      const int kt_per = (KT + splits - 1) / splits;
+      const int ns = (KT + kt_per - 1) / kt_per;  // every split gets at least one stage
+      int32_t* acc32 = MODE == 0 ? acc : static_cast<int32_t*>(out);
+      const unsigned eblocks = (unsigned)std::min<int64_t>((M * N + 255) / 256, 2048);
+      hipLaunchKernelGGL(k_zero32, dim3(eblocks), dim3(256), 0, s, acc32, M * N);
+      const dim3 grid((unsigned)tiles, (unsigned)ns);
+      if (K % BK == 0)
+        hipLaunchKernelGGL((k_gemm<ABITS, BM, BN, WR, WC, BK, MODE, true, true>), grid, dim3(64 * WR * WC), 0, s,
+                           codes, deq, Wq, w_scale, w_scale_up, (int)M, (int)N, (int)K, acc32, out, kt_per);
+      else
+        hipLaunchKernelGGL((k_gemm<ABITS, BM, BN, WR, WC, BK, MODE, false, true>), grid, dim3(64 * WR * WC), 0, s,
+                           codes, deq, Wq, w_scale, w_scale_up, (int)M, (int)N, (int)K, acc32, out, kt_per);
+      if constexpr (MODE == 1)
+        hipLaunchKernelGGL(k_dequant32, dim3(eblocks), dim3(256), 0, s, out, deq, w_scale, M, N);
+      return hipGetLastError();
+    }
+  }
   if (K % BK == 0)
-    hipLaunchKernelGGL((k_gemm<ABITS, BM, BN, WR, WC, BK, MODE, true>), dim3((unsigned)tiles), dim3(64 * WR * WC), 0, s,
-                       codes, deq, Wq, w_scale, w_scale_up, (int)M, (int)N, (int)K, acc, out);
+    hipLaunchKernelGGL((k_gemm<ABITS, BM, BN, WR, WC, BK, MODE, true, false>), dim3((unsigned)tiles),
+                       dim3(64 * WR * WC), 0, s, codes, deq, Wq, w_scale, w_scale_up, (int)M, (int)N, (int)K, acc,
+                       out, KT);
   else
-    hipLaunchKernelGGL((k_gemm<ABITS, BM, BN, WR, WC, BK, MODE, false>), dim3((unsigned)tiles), dim3(64 * WR * WC), 0,
-                       s, codes, deq, Wq, w_scale, w_scale_up, (int)M, (int)N, (int)K, acc, out);
+    hipLaunchKernelGGL((k_gemm<ABITS, BM, BN, WR, WC, BK, MODE, false, false>), dim3((unsigned)tiles),
+                       dim3(64 * WR * WC), 0, s, codes, deq, Wq, w_scale, w_scale_up, (int)M, (int)N, (int)K, acc,
+                       out, KT);
   return hipGetLastError();
 }
+
+constexpr int64_t CUS = 256;
 
 // Tile choice: a 256x256 tile multiplies at roughly twice the rate of a 128x128 tile, so it
 // wins unless it leaves most of the 256 CUs idle.
 inline bool use_big_tiles(int64_t M, int64_t N) {
-  constexpr int64_t CUS = 256;
   const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
   const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
   const double time256 = (double)((t256 + CUS - 1) / CUS) * 4.0 / 2.0;
@@ -387,20 +437,47 @@ inline bool use_big_tiles(int64_t M, int64_t N) {
   return time256 <= time128;
 }
 
+// Tiles and K splits for the product and dequant epilogues.  When the 256 x 256 tiles fill the
+// CUs, or nearly (at least 192 tiles), they run unsplit.  Below that the 128 x 128 tiles run
+// (several fit on a CU), and K is split when there are few of them: the splits add their int32
+// results with atomics, whose cost grows with splits x M x N, so the split count falls as the
+// tile count rises.  Measured at K = 16384, N = 4096 (a4, MI355X), M = 65 ... 4096 against every
+// tile size and 1 to 16 splits, this choice was the fastest or within 3 % of it at each M.
+// Every split keeps at least 8 stages of K.
+struct Plan {
+  bool big;
+  int splits;
+};
+inline Plan plan_tiles(int64_t M, int64_t N, int64_t K) {
+  const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
+  const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
+  if (t256 >= CUS) return Plan{use_big_tiles(M, N), 1};
+  if (t256 >= 3 * CUS / 4) return Plan{true, 1};
+  int64_t splits = t128 <= 32 ? 8 : t128 <= 96 ? 4 : t128 <= 384 ? 2 : 1;
+  splits = std::max<int64_t>(1, std::min<int64_t>(splits, ((K + 127) / 128) / 8));
+  return Plan{false, (int)splits};
+}
+
 template <int ABITS, int MODE>
 hipError_t launch(const uint8_t* codes, const float* deq, const uint8_t* Wq, const float* w_scale,
                   const float* w_scale_up, int64_t M, int64_t K, int64_t N, int32_t* acc, void* out, hipStream_t s) {
   constexpr int BKBIG = ABITS == 4 ? 256 : 128;  // INT8 A tiles are twice as wide in LDS
-  if (use_big_tiles(M, N)) {
-    // The fused SwiGLU epilogue is long (an exp and a division per output), so the gate/up
-    // GEMM runs 128 x 256 tiles with four waves: two blocks share a CU and one block's
-    // epilogue overlaps the other's MFMAs.
-    if constexpr (MODE >= 2)
-      return launch_cfg<ABITS, 128, 256, 1, 4, BKBIG, MODE>(codes, deq, Wq, w_scale, w_scale_up, M, K, N, acc, out, s);
-    else
-      return launch_cfg<ABITS, 256, 256, 2, 4, BKBIG, MODE>(codes, deq, Wq, w_scale, w_scale_up, M, K, N, acc, out, s);
+  if constexpr (MODE >= 2) {
+    // The fused SwiGLU epilogue runs after the whole K, so the gate/up GEMM does not split;
+    // with large problems it runs 128 x 256 tiles with four waves: two blocks share a CU and
+    // one block's epilogue and start-up overlap the other's MFMAs.
+    if (use_big_tiles(M, N))
+      return launch_cfg<ABITS, 128, 256, 1, 4, BKBIG, MODE>(codes, deq, Wq, w_scale, w_scale_up, M, K, N, acc, out, 1,
+                                                            s);
+    return launch_cfg<ABITS, 128, 128, 2, 2, 128, MODE>(codes, deq, Wq, w_scale, w_scale_up, M, K, N, acc, out, 1, s);
+  } else {
+    const Plan p = plan_tiles(M, N, K);
+    if (p.big)
+      return launch_cfg<ABITS, 256, 256, 2, 4, BKBIG, MODE>(codes, deq, Wq, w_scale, w_scale_up, M, K, N, acc, out,
+                                                            p.splits, s);
+    return launch_cfg<ABITS, 128, 128, 2, 2, 128, MODE>(codes, deq, Wq, w_scale, w_scale_up, M, K, N, acc, out,
+                                                        p.splits, s);
   }
-  return launch_cfg<ABITS, 128, 128, 2, 2, 128, MODE>(codes, deq, Wq, w_scale, w_scale_up, M, K, N, acc, out, s);
 }
 
 }  // namespace

@@ -115,13 +115,15 @@ def test_actquant_plain_bitlinear(orc, K, abits):
     _act_case(orc, x, abits, False, norm=False)
 
 
-# Tile configurations: 128 x 128 tiles for the small problems, 256 x 256 for (2500, *, 2200) and
-# (2100, *, 2060); K = 64, 320, 384 and 576 leave a partial last stage (masked loads), the other
-# K fill every stage.  The 256 x 256 cases run 1 to 8 stages (INT4: 256 deep, INT8: 128 deep),
-# odd and even counts, so the two-stage-ahead load pipeline is exercised at its start and end.
+# Tile configurations: 256 x 256 tiles for (3100, *, 4000) (at least 192 of them), 128 x 128
+# tiles for the other problems above 64 rows (the decode kernel below); K = 64, 320, 384 and 576
+# leave a partial last stage (masked loads), the other K fill every stage.  The cases run 1 to 8
+# stages (INT4: 256 deep on the large tiles, otherwise 128), odd and even counts, so the
+# two-stage-ahead load pipeline is exercised at its start and end.
 @pytest.mark.parametrize("M,K,N", [(1, 64, 1), (16, 256, 256), (200, 320, 136), (129, 1024, 257), (300, 2048, 520),
                                    (64, 16384, 64), (2500, 576, 2200), (2500, 1024, 2200), (2100, 64, 2060),
-                                   (2100, 256, 2060), (2100, 384, 2060), (2100, 768, 2060)])
+                                   (2100, 256, 2060), (2100, 384, 2060), (2100, 768, 2060), (3100, 64, 4000),
+                                   (3100, 384, 4000), (3100, 768, 4000)])
 @pytest.mark.parametrize("abits", [4, 8])
 def test_gemm_s32_bit_exact(orc, M, K, N, abits):
     note("gemm_s32", M, K, N, abits)
@@ -131,6 +133,37 @@ def test_gemm_s32_bit_exact(orc, M, K, N, abits):
     T = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
     acc = to_host(B.gemm_s32(to_dev(orc.pack_codes(q, abits)), to_dev(orc.pack_weights(T)), K, abits))
     np.testing.assert_array_equal(acc, orc.gemm_s32(q, T))
+
+
+# Mid-size problems whose tiles alone leave CUs idle split K over several blocks that add
+# their int32 results atomically: 8 splits of 16 stages, 4 splits of 16, and 8 splits of 9
+# stages whose last has only 2, the second of them partial (K = 8320).
+@pytest.mark.parametrize("M,K,N", [(128, 16384, 1024), (1000, 8192, 600), (300, 8320, 520)])
+@pytest.mark.parametrize("abits", [4, 8])
+def test_gemm_s32_split_k(orc, M, K, N, abits):
+    note("gemm_s32 split K", M, K, N, abits)
+    rng = np.random.default_rng(M + K + N)
+    Qb = 7 if abits == 4 else 127
+    q = rng.integers(-Qb - 1, Qb + 1, size=(M, K)).astype(np.int8)
+    T = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+    acc = to_host(B.gemm_s32(to_dev(orc.pack_codes(q, abits)), to_dev(orc.pack_weights(T)), K, abits))
+    np.testing.assert_array_equal(acc, orc.gemm_s32(q, T))
+
+
+@pytest.mark.parametrize("abits", [4, 8])
+def test_gemm_dequant_split_k(orc, abits):
+    M, K, N = 200, 16384, 520
+    note("gemm_dequant split K", M, K, N, abits)
+    rng = np.random.default_rng(abits + 7)
+    Qb = 7 if abits == 4 else 127
+    q = rng.integers(-Qb, Qb + 1, size=(M, K)).astype(np.int8)
+    T = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+    deq = rng.uniform(1e-4, 3.0, M).astype(np.float32)
+    alpha = np.float32(0.0123)
+    torch = torch_mod()
+    y = B.gemm_dequant(to_dev(orc.pack_codes(q, abits)), to_dev(deq), to_dev(orc.pack_weights(T)),
+                       torch.tensor([alpha], device="cuda"), K, abits)
+    np.testing.assert_array_equal(to_host(y), orc.dequant(orc.gemm_s32(q, T), deq, float(alpha)))
 
 
 def test_gemm_s32_extremes(orc):
