@@ -380,13 +380,17 @@ __global__ __launch_bounds__(256) void k_zero32(int32_t* __restrict__ p, int64_t
 }
 
 // In place: the int32 product acc[m, n] -> y[m, n] = fl(fl((float)acc * deq[m]) * alpha).
+// Rows run over blockIdx.y and columns over blockIdx.x (grid-stride in both).
 __global__ __launch_bounds__(256) void k_dequant32(void* __restrict__ buf, const float* __restrict__ deq,
                                                    const float* __restrict__ w_scale, int64_t M, int64_t N) {
   const float alpha = w_scale[0];
-  int32_t* acc = static_cast<int32_t*>(buf);
-  float* y = static_cast<float*>(buf);
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < M * N; i += (int64_t)gridDim.x * 256)
-    y[i] = __fmul_rn(__fmul_rn((float)acc[i], deq[i / N]), alpha);
+  for (int64_t m = blockIdx.y; m < M; m += gridDim.y) {
+    const float dm = deq[m];
+    const int32_t* acc = static_cast<const int32_t*>(buf) + m * N;
+    float* y = static_cast<float*>(buf) + m * N;
+    for (int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x; n < N; n += (int64_t)gridDim.x * 256)
+      y[n] = __fmul_rn(__fmul_rn((float)acc[n], dm), alpha);
+  }
 }
 
 template <int ABITS, int BM, int BN, int WR, int WC, int BK, int MODE>
@@ -410,7 +414,9 @@ hipError_t launch_cfg(const uint8_t* codes, const float* deq, const uint8_t* Wq,
         hipLaunchKernelGGL((k_gemm<ABITS, BM, BN, WR, WC, BK, MODE, false, true>), grid, dim3(64 * WR * WC), 0, s,
                            codes, deq, Wq, w_scale, w_scale_up, (int)M, (int)N, (int)K, acc32, out, kt_per);
       if constexpr (MODE == 1)
-        hipLaunchKernelGGL(k_dequant32, dim3(eblocks), dim3(256), 0, s, out, deq, w_scale, M, N);
+        hipLaunchKernelGGL(k_dequant32, dim3((unsigned)std::min<int64_t>((N + 255) / 256, 64),
+                                             (unsigned)std::min<int64_t>(M, 1024)),
+                           dim3(256), 0, s, out, deq, w_scale, M, N);
       return hipGetLastError();
     }
   }
