@@ -30,6 +30,20 @@ hipError_t launch_decode_fused(const void* x, int xt, int64_t M, int64_t K, int 
 hipError_t launch_gemm(const uint8_t* codes, const float* deq, const uint8_t* Wq, const float* w_scale,
                        int64_t M, int64_t K, int64_t N, int abits, int32_t* acc, float* y, hipStream_t s);
 
+// Tile size and K splits of the tiled GEMMs (k_gemm.hip): 256 x 256 tiles (big) or 128 x 128,
+// and the number of blocks that share each tile's K (their int32 results added atomically).
+constexpr int64_t CUS = 256;
+struct GemmPlan {
+  bool big;
+  int splits;
+};
+bool use_big_tiles(int64_t M, int64_t N);
+GemmPlan plan_tiles(int64_t M, int64_t N, int64_t K);
+// Split-K helpers (k_gemm.hip): zero n int32, and dequantise an int32 product in place
+// (y[m, n] = fl(fl((float)acc[m, n] * deq[m]) * w_scale[0]), same bits as the epilogue).
+hipError_t launch_zero32(int32_t* p, int64_t n, hipStream_t s);
+hipError_t launch_dequant32(void* buf, const float* deq, const float* w_scale, int64_t M, int64_t N, hipStream_t s);
+
 // Decode-regime GEMM for M <= GEMV_MAX_M token rows (k_gemv.hip); launch_gemm dispatches to it.
 constexpr int64_t GEMV_MAX_M = 64;
 hipError_t launch_gemv(const uint8_t* codes, const float* deq, const uint8_t* Wq, const float* w_scale,

@@ -373,8 +373,95 @@ __global__ __launch_bounds__(64 * WR * WC) __attribute__((amdgpu_waves_per_eu(2)
   }
 }
 
+template <int ABITS, int BM, int BN, int WR, int WC, int BK, int MODE>
+hipError_t launch_cfg(const uint8_t* codes, const float* deq, const uint8_t* Wq, const float* w_scale,
+                      const float* w_scale_up, int64_t M, int64_t K, int64_t N, int32_t* acc, void* out,
+                      int splits, hipStream_t s) {
+  const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const int KT = (int)((K + BK - 1) / BK);
+  if constexpr (MODE <= 1) {
+    if (splits > 1) {
+      const int kt_per = (KT + splits - 1) / splits;
+      const int ns = (KT + kt_per - 1) / kt_per;  // every split gets at least one stage
+      int32_t* acc32 = MODE == 0 ? acc : static_cast<int32_t*>(out);
+      if (const hipError_t e = launch_zero32(acc32, M * N, s); e != hipSuccess) return e;
+      const dim3 grid((unsigned)tiles, (unsigned)ns);
+      if (K % BK == 0)
+        hipLaunchKernelGGL((k_gemm<ABITS, BM, BN, WR, WC, BK, MODE, true, true>), grid, dim3(64 * WR * WC), 0, s,
+                           codes, deq, Wq, w_scale, w_scale_up, (int)M, (int)N, (int)K, acc32, out, kt_per);
+      else
+        hipLaunchKernelGGL((k_gemm<ABITS, BM, BN, WR, WC, BK, MODE, false, true>), grid, dim3(64 * WR * WC), 0, s,
+                           codes, deq, Wq, w_scale, w_scale_up, (int)M, (int)N, (int)K, acc32, out, kt_per);
+      if (const hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+      if constexpr (MODE == 1) return launch_dequant32(out, deq, w_scale, M, N, s);
+      return hipSuccess;
+    }
+  }
+  if (K % BK == 0)
+    hipLaunchKernelGGL((k_gemm<ABITS, BM, BN, WR, WC, BK, MODE, true, false>), dim3((unsigned)tiles),
+                       dim3(64 * WR * WC), 0, s, codes, deq, Wq, w_scale, w_scale_up, (int)M, (int)N, (int)K, acc,
+                       out, KT);
+  else
+    hipLaunchKernelGGL((k_gemm<ABITS, BM, BN, WR, WC, BK, MODE, false, false>), dim3((unsigned)tiles),
+                       dim3(64 * WR * WC), 0, s, codes, deq, Wq, w_scale, w_scale_up, (int)M, (int)N, (int)K, acc,
+                       out, KT);
+  return hipGetLastError();
+}
+
+template <int ABITS, int MODE>
+hipError_t launch(const uint8_t* codes, const float* deq, const uint8_t* Wq, const float* w_scale,
+                  const float* w_scale_up, int64_t M, int64_t K, int64_t N, int32_t* acc, void* out, hipStream_t s) {
+  constexpr int BKBIG = ABITS == 4 ? 256 : 128;  // INT8 A tiles are twice as wide in LDS
+  if constexpr (MODE >= 2) {
+    // The fused SwiGLU epilogue runs after the whole K, so the gate/up GEMM does not split;
+    // with large problems it runs 128 x 256 tiles with four waves: two blocks share a CU and
+    // one block's epilogue and start-up overlap the other's MFMAs.
+    if (use_big_tiles(M, N))
+      return launch_cfg<ABITS, 128, 256, 1, 4, BKBIG, MODE>(codes, deq, Wq, w_scale, w_scale_up, M, K, N, acc, out, 1,
+                                                            s);
+    return launch_cfg<ABITS, 128, 128, 2, 2, 128, MODE>(codes, deq, Wq, w_scale, w_scale_up, M, K, N, acc, out, 1, s);
+  } else {
+    const GemmPlan p = plan_tiles(M, N, K);
+    if (p.big)
+      return launch_cfg<ABITS, 256, 256, 2, 4, BKBIG, MODE>(codes, deq, Wq, w_scale, w_scale_up, M, K, N, acc, out,
+                                                            p.splits, s);
+    return launch_cfg<ABITS, 128, 128, 2, 2, 128, MODE>(codes, deq, Wq, w_scale, w_scale_up, M, K, N, acc, out,
+                                                        p.splits, s);
+  }
+}
+
+}  // namespace
+
+// Tile choice: a 256x256 tile multiplies at roughly twice the rate of a 128x128 tile, so it
+// wins unless it leaves most of the 256 CUs idle.
+bool use_big_tiles(int64_t M, int64_t N) {
+  const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
+  const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
+  const double time256 = (double)((t256 + CUS - 1) / CUS) * 4.0 / 2.0;
+  const double time128 = (double)((t128 + CUS - 1) / CUS) * 1.0;
+  return time256 <= time128;
+}
+
+// Tiles and K splits for the product and dequant epilogues.  When the 256 x 256 tiles fill the
+// CUs, or nearly (at least 192 tiles), they run unsplit.  Below that the 128 x 128 tiles run
+// (several fit on a CU), and K is split when there are few of them: the splits add their int32
+// results with atomics, whose cost grows with splits x M x N, so the split count falls as the
+// tile count rises.  Measured at K = 16384, N = 4096 (a4, MI355X), M = 65 ... 4096 against every
+// tile size and 1 to 16 splits, this choice was the fastest or within 3 % of it at each M.
+// Every split keeps at least 8 stages of K.
+GemmPlan plan_tiles(int64_t M, int64_t N, int64_t K) {
+  const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
+  const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
+  if (t256 >= CUS) return GemmPlan{use_big_tiles(M, N), 1};
+  if (t256 >= 3 * CUS / 4) return GemmPlan{true, 1};
+  int64_t splits = t128 <= 32 ? 8 : t128 <= 96 ? 4 : t128 <= 384 ? 2 : 1;
+  splits = std::max<int64_t>(1, std::min<int64_t>(splits, ((K + 127) / 128) / 8));
+  return GemmPlan{false, (int)splits};
+}
+
 // Zero n int32 (split-K accumulators; a kernel rather than a memset so that the sequence can
 // be captured in a graph).
+namespace {
 __global__ __launch_bounds__(256) void k_zero32(int32_t* __restrict__ p, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0;
 }
@@ -392,101 +479,18 @@ __global__ __launch_bounds__(256) void k_dequant32(void* __restrict__ buf, const
       y[n] = __fmul_rn(__fmul_rn((float)acc[n], dm), alpha);
   }
 }
+}  // namespace
 
-template <int ABITS, int BM, int BN, int WR, int WC, int BK, int MODE>
-hipError_t launch_cfg(const uint8_t* codes, const float* deq, const uint8_t* Wq, const float* w_scale,
-                      const float* w_scale_up, int64_t M, int64_t K, int64_t N, int32_t* acc, void* out,
-                      int splits, hipStream_t s) {
-  const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  const int KT = (int)((K + BK - 1) / BK);
-  if constexpr (MODE <= 1) {
-    if (splits > 1) {
-      const int kt_per = (KT + splits - 1) / splits;
-      const int ns = (KT + kt_per - 1) / kt_per;  // every split gets at least one stage
-      int32_t* acc32 = MODE == 0 ? acc : static_cast<int32_t*>(out);
-      const unsigned eblocks = (unsigned)std::min<int64_t>((M * N + 255) / 256, 2048);
-      hipLaunchKernelGGL(k_zero32, dim3(eblocks), dim3(256), 0, s, acc32, M * N);
-      const dim3 grid((unsigned)tiles, (unsigned)ns);
-      if (K % BK == 0)
-        hipLaunchKernelGGL((k_gemm<ABITS, BM, BN, WR, WC, BK, MODE, true, true>), grid, dim3(64 * WR * WC), 0, s,
-                           codes, deq, Wq, w_scale, w_scale_up, (int)M, (int)N, (int)K, acc32, out, kt_per);
-      else
-        hipLaunchKernelGGL((k_gemm<ABITS, BM, BN, WR, WC, BK, MODE, false, true>), grid, dim3(64 * WR * WC), 0, s,
-                           codes, deq, Wq, w_scale, w_scale_up, (int)M, (int)N, (int)K, acc32, out, kt_per);
-      if constexpr (MODE == 1)
-        hipLaunchKernelGGL(k_dequant32, dim3((unsigned)std::min<int64_t>((N + 255) / 256, 64),
-                                             (unsigned)std::min<int64_t>(M, 1024)),
-                           dim3(256), 0, s, out, deq, w_scale, M, N);
-      return hipGetLastError();
-    }
-  }
-  if (K % BK == 0)
-    hipLaunchKernelGGL((k_gemm<ABITS, BM, BN, WR, WC, BK, MODE, true, false>), dim3((unsigned)tiles),
-                       dim3(64 * WR * WC), 0, s, codes, deq, Wq, w_scale, w_scale_up, (int)M, (int)N, (int)K, acc,
-                       out, KT);
-  else
-    hipLaunchKernelGGL((k_gemm<ABITS, BM, BN, WR, WC, BK, MODE, false, false>), dim3((unsigned)tiles),
-                       dim3(64 * WR * WC), 0, s, codes, deq, Wq, w_scale, w_scale_up, (int)M, (int)N, (int)K, acc,
-                       out, KT);
+hipError_t launch_zero32(int32_t* p, int64_t n, hipStream_t s) {
+  hipLaunchKernelGGL(k_zero32, dim3((unsigned)std::min<int64_t>((n + 255) / 256, 2048)), dim3(256), 0, s, p, n);
   return hipGetLastError();
 }
 
-constexpr int64_t CUS = 256;
-
-// Tile choice: a 256x256 tile multiplies at roughly twice the rate of a 128x128 tile, so it
-// wins unless it leaves most of the 256 CUs idle.
-inline bool use_big_tiles(int64_t M, int64_t N) {
-  const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
-  const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
-  const double time256 = (double)((t256 + CUS - 1) / CUS) * 4.0 / 2.0;
-  const double time128 = (double)((t128 + CUS - 1) / CUS) * 1.0;
-  return time256 <= time128;
+hipError_t launch_dequant32(void* buf, const float* deq, const float* w_scale, int64_t M, int64_t N, hipStream_t s) {
+  hipLaunchKernelGGL(k_dequant32, dim3((unsigned)std::min<int64_t>((N + 255) / 256, 64), (unsigned)std::min<int64_t>(M, 1024)),
+                     dim3(256), 0, s, buf, deq, w_scale, M, N);
+  return hipGetLastError();
 }
-
-// Tiles and K splits for the product and dequant epilogues.  When the 256 x 256 tiles fill the
-// CUs, or nearly (at least 192 tiles), they run unsplit.  Below that the 128 x 128 tiles run
-// (several fit on a CU), and K is split when there are few of them: the splits add their int32
-// results with atomics, whose cost grows with splits x M x N, so the split count falls as the
-// tile count rises.  Measured at K = 16384, N = 4096 (a4, MI355X), M = 65 ... 4096 against every
-// tile size and 1 to 16 splits, this choice was the fastest or within 3 % of it at each M.
-// Every split keeps at least 8 stages of K.
-struct Plan {
-  bool big;
-  int splits;
-};
-inline Plan plan_tiles(int64_t M, int64_t N, int64_t K) {
-  const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
-  const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
-  if (t256 >= CUS) return Plan{use_big_tiles(M, N), 1};
-  if (t256 >= 3 * CUS / 4) return Plan{true, 1};
-  int64_t splits = t128 <= 32 ? 8 : t128 <= 96 ? 4 : t128 <= 384 ? 2 : 1;
-  splits = std::max<int64_t>(1, std::min<int64_t>(splits, ((K + 127) / 128) / 8));
-  return Plan{false, (int)splits};
-}
-
-template <int ABITS, int MODE>
-hipError_t launch(const uint8_t* codes, const float* deq, const uint8_t* Wq, const float* w_scale,
-                  const float* w_scale_up, int64_t M, int64_t K, int64_t N, int32_t* acc, void* out, hipStream_t s) {
-  constexpr int BKBIG = ABITS == 4 ? 256 : 128;  // INT8 A tiles are twice as wide in LDS
-  if constexpr (MODE >= 2) {
-    // The fused SwiGLU epilogue runs after the whole K, so the gate/up GEMM does not split;
-    // with large problems it runs 128 x 256 tiles with four waves: two blocks share a CU and
-    // one block's epilogue and start-up overlap the other's MFMAs.
-    if (use_big_tiles(M, N))
-      return launch_cfg<ABITS, 128, 256, 1, 4, BKBIG, MODE>(codes, deq, Wq, w_scale, w_scale_up, M, K, N, acc, out, 1,
-                                                            s);
-    return launch_cfg<ABITS, 128, 128, 2, 2, 128, MODE>(codes, deq, Wq, w_scale, w_scale_up, M, K, N, acc, out, 1, s);
-  } else {
-    const Plan p = plan_tiles(M, N, K);
-    if (p.big)
-      return launch_cfg<ABITS, 256, 256, 2, 4, BKBIG, MODE>(codes, deq, Wq, w_scale, w_scale_up, M, K, N, acc, out,
-                                                            p.splits, s);
-    return launch_cfg<ABITS, 128, 128, 2, 2, 128, MODE>(codes, deq, Wq, w_scale, w_scale_up, M, K, N, acc, out,
-                                                        p.splits, s);
-  }
-}
-
-}  // namespace
 
 hipError_t launch_gemm(const uint8_t* codes, const float* deq, const uint8_t* Wq, const float* w_scale, int64_t M,
                        int64_t K, int64_t N, int abits, int32_t* acc, float* y, hipStream_t s) {

@@ -47,12 +47,15 @@ __device__ __forceinline__ void tile_order(int bid, int nblk, int ntm, int ntn, 
   tn = r / gm;
 }
 
-template <int BM, int BN, int WR, int WC, int MODE, bool FULLK>
+// SPLIT: the block multiplies only the stages [blockIdx.y * kt_per, + kt_per) of K and adds
+// its integer result into acc_out with atomics, as the int8 GEMM does for mid-size problems.
+template <int BM, int BN, int WR, int WC, int MODE, bool FULLK, bool SPLIT>
 __global__ __launch_bounds__(64 * WR * WC) void k_gemm_f6f4(const uint8_t* __restrict__ A,
                                                             const float* __restrict__ deq,
                                                             const uint8_t* __restrict__ B,
                                                             const float* __restrict__ w_scale, int M, int N, int K,
-                                                            int32_t* __restrict__ acc_out, float* __restrict__ y) {
+                                                            int32_t* __restrict__ acc_out, float* __restrict__ y,
+                                                            int kt_per) {
   constexpr int NT = 64 * WR * WC;
   constexpr int KS = BK6 / 64;                // 64-deep MFMA steps per stage
   constexpr int AB = BK6 * 6 / 8;             // 96 bytes of FP6 codes per row per stage
@@ -79,6 +82,8 @@ __global__ __launch_bounds__(64 * WR * WC) void k_gemm_f6f4(const uint8_t* __res
   const int64_t brow = K / 2;
   const int KT = (K + BK6 - 1) / BK6;
   const int last_k64 = (K - (KT - 1) * BK6) / 64;
+  const int kb = SPLIT ? (int)blockIdx.y * kt_per : 0;   // this block's first stage
+  const int KTL = SPLIT ? min(KT - kb, kt_per) : KT;     // and its number of stages
 
   const uint8_t* Ablk = A + (int64_t)m0 * arow;
   const uint8_t* Bblk = B + (int64_t)n0 * brow;
@@ -223,7 +228,7 @@ __global__ __launch_bounds__(64 * WR * WC) void k_gemm_f6f4(const uint8_t* __res
   auto stage = [&](auto S, int kt) __attribute__((always_inline)) {
     constexpr int set = decltype(S)::value;
     const int buf = kt & 1;
-    const int nx = min(kt + 2, KT - 1);
+    const int nx = kb + min(kt + 2, KTL - 1);  // kt counts this block's stages
     gload(S, nx, nx == KT - 1 ? last_k64 : KS);
     fread(buf, 1, f1);
     fmma(f0);
@@ -243,18 +248,18 @@ __global__ __launch_bounds__(64 * WR * WC) void k_gemm_f6f4(const uint8_t* __res
     __syncthreads();
     fread(buf ^ 1, 0, f0);
   };
-  gload(I0{}, 0, KT == 1 ? last_k64 : KS);
-  const int n1 = min(1, KT - 1);
+  gload(I0{}, kb, kb == KT - 1 ? last_k64 : KS);
+  const int n1 = kb + min(1, KTL - 1);
   gload(I1{}, n1, n1 == KT - 1 ? last_k64 : KS);
   swrite(I0{}, 0);
   __syncthreads();
   fread(0, 0, f0);
   int kt = 0;
-  for (; kt + 1 < KT; kt += 2) {
+  for (; kt + 1 < KTL; kt += 2) {
     stage(I0{}, kt);
     stage(I1{}, kt + 1);
   }
-  if (kt < KT) stage(I0{}, kt);
+  if (kt < KTL) stage(I0{}, kt);
 
   // The epilogue takes the lane index afresh (v_mbcnt) rather than keeping the main loop's
   // lane-derived values live across it, which at 128 VGPRs made the compiler spill them.
@@ -274,7 +279,9 @@ __global__ __launch_bounds__(64 * WR * WC) void k_gemm_f6f4(const uint8_t* __res
         const int n = n0 + wn * WN + 32 * j + (el & 31);
         if (n >= N) continue;
         const float a = acc[i][j][v];  // an exact integer
-        if constexpr (MODE == 0) {
+        if constexpr (SPLIT) {
+          atomicAdd(&acc_out[(int64_t)m * N + n], (int32_t)a);
+        } else if constexpr (MODE == 0) {
           acc_out[(int64_t)m * N + n] = (int32_t)a;
         } else {
           y[(int64_t)m * N + n] = __fmul_rn(__fmul_rn(a, dm), alpha);
@@ -286,26 +293,42 @@ __global__ __launch_bounds__(64 * WR * WC) void k_gemm_f6f4(const uint8_t* __res
 
 template <int BM, int BN, int WR, int WC, int MODE>
 hipError_t launch_cfg(const uint8_t* codes, const float* deq, const uint8_t* Wq4, const float* w_scale, int64_t M,
-                      int64_t K, int64_t N, int32_t* acc, float* y, hipStream_t s) {
+                      int64_t K, int64_t N, int32_t* acc, float* y, int splits, hipStream_t s) {
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const int KT = (int)((K + BK6 - 1) / BK6);
+  if (splits > 1) {
+    const int kt_per = (KT + splits - 1) / splits;
+    const int ns = (KT + kt_per - 1) / kt_per;  // every split gets at least one stage
+    int32_t* acc32 = MODE == 0 ? acc : reinterpret_cast<int32_t*>(y);
+    if (const hipError_t e = launch_zero32(acc32, M * N, s); e != hipSuccess) return e;
+    const dim3 grid((unsigned)tiles, (unsigned)ns);
+    if (K % BK6 == 0)
+      hipLaunchKernelGGL((k_gemm_f6f4<BM, BN, WR, WC, MODE, true, true>), grid, dim3(64 * WR * WC), 0, s, codes, deq,
+                         Wq4, w_scale, (int)M, (int)N, (int)K, acc32, y, kt_per);
+    else
+      hipLaunchKernelGGL((k_gemm_f6f4<BM, BN, WR, WC, MODE, false, true>), grid, dim3(64 * WR * WC), 0, s, codes, deq,
+                         Wq4, w_scale, (int)M, (int)N, (int)K, acc32, y, kt_per);
+    if (const hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    if constexpr (MODE == 1) return launch_dequant32(y, deq, w_scale, M, N, s);
+    return hipSuccess;
+  }
   if (K % BK6 == 0)
-    hipLaunchKernelGGL((k_gemm_f6f4<BM, BN, WR, WC, MODE, true>), dim3((unsigned)tiles), dim3(64 * WR * WC), 0, s,
-                       codes, deq, Wq4, w_scale, (int)M, (int)N, (int)K, acc, y);
+    hipLaunchKernelGGL((k_gemm_f6f4<BM, BN, WR, WC, MODE, true, false>), dim3((unsigned)tiles), dim3(64 * WR * WC), 0,
+                       s, codes, deq, Wq4, w_scale, (int)M, (int)N, (int)K, acc, y, KT);
   else
-    hipLaunchKernelGGL((k_gemm_f6f4<BM, BN, WR, WC, MODE, false>), dim3((unsigned)tiles), dim3(64 * WR * WC), 0, s,
-                       codes, deq, Wq4, w_scale, (int)M, (int)N, (int)K, acc, y);
+    hipLaunchKernelGGL((k_gemm_f6f4<BM, BN, WR, WC, MODE, false, false>), dim3((unsigned)tiles), dim3(64 * WR * WC), 0,
+                       s, codes, deq, Wq4, w_scale, (int)M, (int)N, (int)K, acc, y, KT);
   return hipGetLastError();
 }
 
+// The tile size and K splits follow the int8 GEMM's plan (plan_tiles): 256 x 256 tiles when
+// they (nearly) fill the CUs, else 128 x 128 tiles with K split when those are few.
 template <int MODE>
 hipError_t launch(const uint8_t* codes, const float* deq, const uint8_t* Wq4, const float* w_scale, int64_t M,
                   int64_t K, int64_t N, int32_t* acc, float* y, hipStream_t s) {
-  constexpr int64_t CUS = 256;
-  const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
-  const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
-  if ((double)((t256 + CUS - 1) / CUS) * 2.0 <= (double)((t128 + CUS - 1) / CUS))
-    return launch_cfg<256, 256, 4, 2, MODE>(codes, deq, Wq4, w_scale, M, K, N, acc, y, s);
-  return launch_cfg<128, 128, 2, 2, MODE>(codes, deq, Wq4, w_scale, M, K, N, acc, y, s);
+  const GemmPlan p = plan_tiles(M, N, K);
+  if (p.big) return launch_cfg<256, 256, 4, 2, MODE>(codes, deq, Wq4, w_scale, M, K, N, acc, y, p.splits, s);
+  return launch_cfg<128, 128, 2, 2, MODE>(codes, deq, Wq4, w_scale, M, K, N, acc, y, p.splits, s);
 }
 
 // Ternary 2-bit words (16 weights, weight c in field 4(c%4)+c/4) -> FP4 E2M1 nibbles in

@@ -47,9 +47,12 @@ def test_actquant_fp6_plain(orc, K):
 
 # K = 64, 320, 576: partial last stage (masked loads); the others fill every 128-deep stage.
 # An odd number of stages (K = 64, 320, 576, 1152) ends on the loop's peeled last stage.
+# (3100, *, 4000) runs 256 x 256 tiles; the others 128 x 128, and (64, 16384, 64), (128, 16384,
+# 1024) and (300, 8320, 520) split K (the last with a partial last stage in its last split).
 @pytest.mark.parametrize("M,K,N", [(1, 64, 1), (200, 320, 136), (129, 1024, 257), (64, 16384, 64),
                                    (2500, 576, 2200), (2500, 1152, 2200), (2100, 64, 2060), (2100, 256, 2060),
-                                   (2100, 384, 2060)])
+                                   (2100, 384, 2060), (3100, 64, 4000), (3100, 384, 4000), (128, 16384, 1024),
+                                   (300, 8320, 520)])
 def test_gemm_fp6fp4_s32(orc, M, K, N):
     note("gemm fp6fp4", M, K, N)
     rng = np.random.default_rng(M + N)
