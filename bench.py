@@ -303,8 +303,8 @@ def main():
                "kernels_us": {"actquant_fwht_fp6": ta6 * 1e6, "gemm_fp6fp4_dequant": tg6 * 1e6},
                "roofline": {"bound": "mfma", "achieved": g6, "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s",
                             "frac": g6 / PEAK_FP4_TFLOPS,
-                            "traffic": measured_traffic("k_gemm_f6f4<256, 256, 4, 2, 1, true>"),
-                            "kernel": "k_gemm_f6f4<256, 256, 4, 2, 1, true>",
+                            "traffic": measured_traffic("k_gemm_f6f4<256, 256, 4, 2, 1, true, false>"),
+                            "kernel": "k_gemm_f6f4<256, 256, 4, 2, 1, true, false>",
                             "algorithmic": "2*M*N*K ops per launch"},
                "mfma_ceiling": None if not ceil6 else {
                    "tflops": ceil6, "frac_of_peak": ceil6 / PEAK_FP4_TFLOPS, "gemm_frac_of_ceiling": g6 / ceil6,
