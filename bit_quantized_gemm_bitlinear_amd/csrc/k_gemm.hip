@@ -37,6 +37,7 @@
 // the same lanes; the epilogue dequantises both with their own weight scales and stores
 // h = silu(g) * u once (fp32 for 2, bf16 for 3) instead of writing g and u.
 #include <algorithm>
+#include <cmath>
 #include <type_traits>
 
 #include "hbl_device.h"
@@ -444,18 +445,23 @@ bool use_big_tiles(int64_t M, int64_t N) {
 
 // Tiles and K splits for the product and dequant epilogues.  When the 256 x 256 tiles fill the
 // CUs, or nearly (at least 192 tiles), they run unsplit.  Below that the 128 x 128 tiles run
-// (several fit on a CU), and K is split when there are few of them: the splits add their int32
-// results with atomics, whose cost grows with splits x M x N, so the split count falls as the
-// tile count rises.  Measured at K = 16384, N = 4096 (a4, MI355X), M = 65 ... 4096 against every
-// tile size and 1 to 16 splits, this choice was the fastest or within 3 % of it at each M.
-// Every split keeps at least 8 stages of K.
+// (several fit on a CU), and K may be split: the splits add their int32 results with atomics,
+// whose cost grows with splits x M x N while each split's multiply time falls as K / splits, so
+// the best count is about sqrt(1024 K / (M N)), taken to the nearest power of two (at most 8,
+// at most two blocks per CU, each split at least 4 stages; no split below 2 when the tiles
+// already fill the CUs).  Against a sweep of K = 2048 ... 16384, N = 4096, M = 65 ... 2048 over
+// both tile sizes and 1 to 16 splits (a4, MI355X) this choice was the fastest or within 4 % of
+// it at 26 of the 28 points, and within 13 % at all.
 GemmPlan plan_tiles(int64_t M, int64_t N, int64_t K) {
   const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
   const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
   if (t256 >= CUS) return GemmPlan{use_big_tiles(M, N), 1};
   if (t256 >= 3 * CUS / 4) return GemmPlan{true, 1};
-  int64_t splits = t128 <= 32 ? 8 : t128 <= 96 ? 4 : t128 <= 384 ? 2 : 1;
-  splits = std::max<int64_t>(1, std::min<int64_t>(splits, ((K + 127) / 128) / 8));
+  const double r = 0.5 * std::log2(1024.0 * (double)K / ((double)M * (double)N));
+  int64_t splits = r <= 0.0 ? 1 : (int64_t)1 << std::min(3, (int)std::floor(r + 0.5));
+  if (t128 >= CUS && r < 1.0) splits = 1;
+  splits = std::min(splits, std::max<int64_t>(1, 2 * CUS / t128));
+  splits = std::max<int64_t>(1, std::min(splits, ((K + 127) / 128) / 4));
   return GemmPlan{false, (int)splits};
 }
 
