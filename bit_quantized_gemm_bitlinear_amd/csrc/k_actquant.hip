@@ -266,6 +266,22 @@ __device__ __forceinline__ void load_chunk(RowChunk<XT>& c, const void* x, int64
   for (int i = 0; i < (XT == 1 ? 8 : 16); ++i) c.w[i] = src[i];
 }
 
+// The same 64 elements taken as 8 chunks of 8 consecutive ones, chunk i at elem0 + 8*T*i:
+// the T threads of a row then read it in fully coalesced 16-byte units.
+template <int XT, int T>
+__device__ __forceinline__ void load_chunk_strided(RowChunk<XT>& c, const void* x, int64_t elem0) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if constexpr (XT == 1) {
+      c.w[i] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + elem0 + 8 * T * i);
+    } else {
+      const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(x) + elem0 + 8 * T * i);
+      c.w[2 * i] = p[0];
+      c.w[2 * i + 1] = p[1];
+    }
+  }
+}
+
 template <int XT>
 __device__ __forceinline__ void unpack_chunk(const RowChunk<XT>& c, float (&v)[64]) {
 #pragma unroll
@@ -292,15 +308,18 @@ __device__ __forceinline__ void unpack_chunk(const RowChunk<XT>& c, float (&v)[6
 // NM: 0 = no norm, 1 = RMSNorm with unit gamma, 2 = RMSNorm with gamma.
 // Blocks are persistent: block b handles row groups b, b + gridDim.x, ...; the raw input of
 // the next group is loaded into registers while the current one is transformed.
-template <int L, int ABITS, int XT, int NM>
-__global__ __launch_bounds__(block_threads<L>()) void k_actquant_h(
+// HT = false skips the transform (the BitLinear path for K = 2^L): each thread then holds 8
+// chunks of 8 consecutive elements, chunk i at row offset 8 (t + T i), so that loads and code
+// stores are coalesced across the row's threads, and quantises them with no LDS exchange.
+template <int L, int ABITS, int XT, int NM, bool HT>
+__device__ __forceinline__ void actquant_rows(
     const void* __restrict__ x, int64_t M, const float* __restrict__ gamma, float eps, float hK,
     uint8_t* __restrict__ codes, float* __restrict__ deq) {
   constexpr int K = 1 << L;
   constexpr int T = K / 64;           // threads per row
   constexpr int WG = block_threads<L>();
   constexpr int R = WG / T;           // rows per block
-  constexpr int NP = nphases(L);
+  constexpr int NP = HT ? nphases(L) : 1;
   constexpr int ROWF = K + K / 16;    // padded floats per LDS row
   constexpr int NW = WG / 64;
   constexpr float Qb = QB<ABITS>::value;
@@ -316,10 +335,11 @@ __global__ __launch_bounds__(block_threads<L>()) void k_actquant_h(
 
   float g[64];
   if constexpr (NM == 2) {
-    const float4* gp = reinterpret_cast<const float4*>(gamma + 64 * t);
+    // gamma in the thread's element order: 64 consecutive, or 8 chunks of 8 (no transform)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float4 q = gp[i];
+      const float4 q = *reinterpret_cast<const float4*>(
+          gamma + (HT ? 64 * t + 4 * i : 8 * t + 8 * T * (i / 2) + 4 * (i % 2)));
       g[4 * i + 0] = q.x;
       g[4 * i + 1] = q.y;
       g[4 * i + 2] = q.z;
@@ -329,12 +349,17 @@ __global__ __launch_bounds__(block_threads<L>()) void k_actquant_h(
 
   RowChunk<XT> cur, nxt;
   int64_t grp = blockIdx.x;
-  if (grp < ngroups) load_chunk<XT>(cur, x, min(grp * R + rl, M - 1) * K + 64 * t);
+  auto load_group = [&](RowChunk<XT>& c, int64_t group) __attribute__((always_inline)) {
+    const int64_t e0 = min(group * R + rl, M - 1) * K;
+    if constexpr (HT) load_chunk<XT>(c, x, e0 + 64 * t);
+    else load_chunk_strided<XT, T>(c, x, e0 + 8 * t);
+  };
+  if (grp < ngroups) load_group(cur, grp);
   for (; grp < ngroups; grp += gridDim.x) {
     const int64_t row = grp * R + rl;
     const bool valid = row < M;        // rows past M are computed from row M-1, never stored
     const int64_t ngrp = grp + gridDim.x;
-    if (ngrp < ngroups) load_chunk<XT>(nxt, x, min(ngrp * R + rl, M - 1) * K + 64 * t);
+    if (ngrp < ngroups) load_group(nxt, ngrp);
 
     float v[64];
     unpack_chunk<XT>(cur, v);
@@ -352,7 +377,7 @@ __global__ __launch_bounds__(block_threads<L>()) void k_actquant_h(
     }
 
     // Phase 0: index bits 0..5 in registers.
-    stages<0, phase_desc(L, 0).a>(v);
+    if constexpr (HT) stages<0, phase_desc(L, 0).a>(v);
     if constexpr (NP > 1) {
       lds_write<L, 0, ROWF>(v, rowlds, t);
       __syncthreads();
@@ -387,9 +412,14 @@ __global__ __launch_bounds__(block_threads<L>()) void k_actquant_h(
       using LY = Layout<L, LASTP>;
       constexpr int RL = NP == 1 ? 64 : (1 << LY::c);  // run of consecutive elements in registers
       const int b = NP == 1 ? 64 * t : LY::base(t);
+      if constexpr (!HT) {
 #pragma unroll
-      for (int gi = 0; gi < 64 / RL; ++gi)
-        store_run<ABITS, RL>(v + gi * RL, s, crow, NP == 1 ? b + gi * RL : b + LY::off(gi * RL));
+        for (int i = 0; i < 8; ++i) store_run<ABITS, 8>(v + 8 * i, s, crow, 8 * (t + T * i));
+      } else {
+#pragma unroll
+        for (int gi = 0; gi < 64 / RL; ++gi)
+          store_run<ABITS, RL>(v + gi * RL, s, crow, NP == 1 ? b + gi * RL : b + LY::off(gi * RL));
+      }
       if (t == 0)
         deq[row] = zero ? 0.0f : __fmul_rn(__fmul_rn(ABITS == 5 ? amax : amax / Qb, r), hK);
     }
@@ -397,6 +427,20 @@ __global__ __launch_bounds__(block_threads<L>()) void k_actquant_h(
     // The next group reuses LDS and the reduction slots: every thread must be done with them.
     __syncthreads();
   }
+}
+
+template <int L, int ABITS, int XT, int NM>
+__global__ __launch_bounds__(block_threads<L>()) void k_actquant_h(
+    const void* __restrict__ x, int64_t M, const float* __restrict__ gamma, float eps, float hK,
+    uint8_t* __restrict__ codes, float* __restrict__ deq) {
+  actquant_rows<L, ABITS, XT, NM, true>(x, M, gamma, eps, hK, codes, deq);
+}
+
+template <int L, int ABITS, int XT, int NM>
+__global__ __launch_bounds__(block_threads<L>()) void k_actquant_pow2(
+    const void* __restrict__ x, int64_t M, const float* __restrict__ gamma, float eps,
+    uint8_t* __restrict__ codes, float* __restrict__ deq) {
+  actquant_rows<L, ABITS, XT, NM, false>(x, M, gamma, eps, 1.0f, codes, deq);
 }
 
 // Decode-regime H-BitLinear forward in one kernel (M <= R token rows, R = rows the block
@@ -758,6 +802,37 @@ hipError_t dispatch_h(int L, const void* x, int64_t M, const float* gamma, float
   }
 }
 
+// BitLinear path for K = 2^L, 2^11 <= K <= 2^14: the persistent row kernel without the
+// transform (64 consecutive elements per thread, reductions in registers and shuffles).
+template <int L, int ABITS, int XT>
+hipError_t launch_pow2(const void* x, int64_t M, const float* gamma, float eps, int norm, uint8_t* codes,
+                       float* deq, hipStream_t s) {
+  constexpr int K = 1 << L;
+  constexpr int R = block_threads<L>() / (K / 64);
+  const int64_t groups = (M + R - 1) / R;
+  const int64_t blocks = groups < 2048 ? groups : 2048;
+  const dim3 grid((unsigned)blocks), block(block_threads<L>());
+  if (!norm)
+    hipLaunchKernelGGL((k_actquant_pow2<L, ABITS, XT, 0>), grid, block, 0, s, x, M, gamma, eps, codes, deq);
+  else if (gamma == nullptr)
+    hipLaunchKernelGGL((k_actquant_pow2<L, ABITS, XT, 1>), grid, block, 0, s, x, M, gamma, eps, codes, deq);
+  else
+    hipLaunchKernelGGL((k_actquant_pow2<L, ABITS, XT, 2>), grid, block, 0, s, x, M, gamma, eps, codes, deq);
+  return hipGetLastError();
+}
+
+template <int ABITS, int XT>
+hipError_t dispatch_pow2(int L, const void* x, int64_t M, const float* gamma, float eps, int norm, uint8_t* codes,
+                         float* deq, hipStream_t s) {
+  switch (L) {
+    case 11: return launch_pow2<11, ABITS, XT>(x, M, gamma, eps, norm, codes, deq, s);
+    case 12: return launch_pow2<12, ABITS, XT>(x, M, gamma, eps, norm, codes, deq, s);
+    case 13: return launch_pow2<13, ABITS, XT>(x, M, gamma, eps, norm, codes, deq, s);
+    case 14: return launch_pow2<14, ABITS, XT>(x, M, gamma, eps, norm, codes, deq, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <int ABITS, int XT>
 hipError_t dispatch_plain(const void* x, int64_t M, int64_t K, const float* gamma, float eps, int norm,
                           uint8_t* codes, float* deq, hipStream_t s) {
@@ -817,6 +892,21 @@ hipError_t launch_actquant(const void* x, int xt, int64_t M, int64_t K, int norm
                 : dispatch_h<5, 0>(L, x, M, gamma, eps, norm, codes, deq, s);
     return xt ? dispatch_h<8, 1>(L, x, M, gamma, eps, norm, codes, deq, s)
               : dispatch_h<8, 0>(L, x, M, gamma, eps, norm, codes, deq, s);
+  }
+  int L = 0;
+  while ((int64_t(1) << L) < K) ++L;
+  if ((int64_t(1) << L) == K && L >= 11 && L <= 14) {
+    if (abits == 4)
+      return xt ? dispatch_pow2<4, 1>(L, x, M, gamma, eps, norm, codes, deq, s)
+                : dispatch_pow2<4, 0>(L, x, M, gamma, eps, norm, codes, deq, s);
+    if (abits == 6)
+      return xt ? dispatch_pow2<6, 1>(L, x, M, gamma, eps, norm, codes, deq, s)
+                : dispatch_pow2<6, 0>(L, x, M, gamma, eps, norm, codes, deq, s);
+    if (abits == 5)
+      return xt ? dispatch_pow2<5, 1>(L, x, M, gamma, eps, norm, codes, deq, s)
+                : dispatch_pow2<5, 0>(L, x, M, gamma, eps, norm, codes, deq, s);
+    return xt ? dispatch_pow2<8, 1>(L, x, M, gamma, eps, norm, codes, deq, s)
+              : dispatch_pow2<8, 0>(L, x, M, gamma, eps, norm, codes, deq, s);
   }
   if (abits == 4)
     return xt ? dispatch_plain<4, 1>(x, M, K, gamma, eps, norm, codes, deq, s)

@@ -115,6 +115,23 @@ def test_actquant_plain_bitlinear(orc, K, abits):
     _act_case(orc, x, abits, False, norm=False)
 
 
+# K = 2^11 .. 2^14 without the transform run the persistent row kernel (8 chunks of 8
+# elements per thread, several rows per block for K < 2^14): ragged row groups, gamma in
+# the chunked element order, bf16 and fp32 inputs.
+@pytest.mark.parametrize("L", [11, 12, 13, 14])
+@pytest.mark.parametrize("abits", [4, 8])
+def test_actquant_plain_pow2_gamma(orc, L, abits):
+    K = 1 << L
+    M = 256 // (K // 64) + 3
+    note("actquant plain pow2 gamma", K, abits, M)
+    x = inputs.make_activations("mixture", M, K, seed=200 + L, outlier_frac=0.01, outlier_scale=50.0)
+    gamma = np.random.default_rng(L).uniform(0.25, 2.0, K).astype(np.float32)
+    _act_case(orc, x, abits, False, norm=True, gamma=gamma)
+    xf = (np.random.default_rng(300 + L).standard_normal((M, K)) * 2).astype(np.float32)
+    _act_case(orc, xf, abits, False, norm=True, gamma=gamma, eps=1e-6)
+    _act_case(orc, xf, abits, False, norm=False)
+
+
 # Tile configurations: 256 x 256 tiles for (3100, *, 4000) (at least 192 of them), 128 x 128
 # tiles for the other problems above 64 rows (the decode kernel below); K = 64, 320, 384 and 576
 # leave a partial last stage (masked loads), the other K fill every stage.  The cases run 1 to 8
