@@ -772,8 +772,13 @@ hipError_t launch_h(const void* x, int64_t M, const float* gamma, float eps, int
   constexpr int R = WG / T;
   const float hK = (float)(1.0 / std::sqrt((double)K));
   const int64_t groups = (M + R - 1) / R;
-  // Persistent blocks: two resident per CU (LDS-limited) on 256 CUs, a few rounds deep.
-  const int64_t blocks = groups < 2048 ? groups : 2048;
+  // Persistent blocks, exactly as many as are resident at once: every block holds about
+  // 68 KB of LDS (one 2^14-float row, or several shorter ones), so two fit in a CU's 160 KB
+  // (one for K = 2^15), and each then walks its share of the row groups with the next
+  // group's input prefetched.  Four times as many blocks, a few rounds of block launches,
+  // measured 5-6 % slower at K = 2^14.
+  const int64_t cap = L <= 14 ? 2 * CUS : CUS;
+  const int64_t blocks = groups < cap ? groups : cap;
   const dim3 grid((unsigned)blocks), block(WG);
   if (!norm)
     hipLaunchKernelGGL((k_actquant_h<L, ABITS, XT, 0>), grid, block, 0, s, x, M, gamma, eps, hK, codes, deq);
