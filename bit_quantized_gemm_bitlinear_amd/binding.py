@@ -113,12 +113,42 @@ def _dev(*ts):
             raise ValueError("tensors must be contiguous and on the GPU")
 
 
+class ShapeError(ValueError):
+    """A tensor whose dtype or shape does not match what the call reads or writes (raised
+    before anything is launched: the C ABI sees only pointers and cannot check extents)."""
+
+
+def _want(t, name: str, dtype=None, shape=None, numel=None, optional: bool = False):
+    """Checks dtype and extent of `t` (None passes when optional)."""
+    import torch
+
+    if t is None:
+        if optional:
+            return
+        raise ShapeError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise ShapeError(f"{name} must be a torch tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ShapeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ShapeError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if numel is not None and t.numel() != numel:
+        raise ShapeError(f"{name} must hold {numel} elements, got {t.numel()}")
+
+
+def _rows(x, name: str):
+    if x.dim() != 2:
+        raise ShapeError(f"{name} must be 2-D, got {x.dim()}-D")
+    return x.shape
+
+
 def quantize_weights(W):
     """W [N, K] fp32 on the GPU -> (Wq uint8 [N, K/4], w_scale fp32 [1])."""
     import torch
 
+    N, K = _rows(W, "W")
+    _want(W, "W", torch.float32)
     _dev(W)
-    N, K = W.shape
     L = lib()
     Wq = torch.empty((N, K // 4), dtype=torch.uint8, device=W.device)
     scale = torch.empty(1, dtype=torch.float32, device=W.device)
@@ -133,8 +163,10 @@ def quantize_activations(x, abits: int, use_hadamard: bool, norm: bool = False, 
     """x [M, K] bf16/fp32 -> (codes uint8 [M, K*abits/8], deq fp32 [M]); stat: absmax / absmean."""
     import torch
 
+    M, K = _rows(x, "x")
+    _xdtype(x)
+    _want(gamma, "gamma", torch.float32, numel=K, optional=True)
     _dev(x, gamma)
-    M, K = x.shape
     codes = torch.empty((M, K * abits // 8), dtype=torch.uint8, device=x.device)
     deq = torch.empty(M, dtype=torch.float32, device=x.device)
     _check(lib().hbl_quantize_activations_stat(_ptr(x), _xdtype(x), M, K, HBL_NORM_RMS if norm else HBL_NORM_NONE,
@@ -147,8 +179,10 @@ def gemm_s32(codes, Wq, K: int, abits: int):
     """codes [M, K*abits/8], Wq [N, K/4] -> acc int32 [M, N] (exact integer product)."""
     import torch
 
+    M, N = _rows(codes, "codes")[0], _rows(Wq, "Wq")[0]
+    _want(codes, "codes", torch.uint8, shape=(M, K * abits // 8))
+    _want(Wq, "Wq", torch.uint8, shape=(N, K // 4))
     _dev(codes, Wq)
-    M, N = codes.shape[0], Wq.shape[0]
     acc = torch.empty((M, N), dtype=torch.int32, device=codes.device)
     _check(lib().hbl_gemm_s32(_ptr(codes), _ptr(Wq), M, K, N, int(abits), _ptr(acc), _stream()))
     return acc
@@ -157,8 +191,13 @@ def gemm_s32(codes, Wq, K: int, abits: int):
 def gemm_dequant(codes, deq, Wq, w_scale, K: int, abits: int, y=None):
     import torch
 
+    M, N = _rows(codes, "codes")[0], _rows(Wq, "Wq")[0]
+    _want(codes, "codes", torch.uint8, shape=(M, K * abits // 8))
+    _want(Wq, "Wq", torch.uint8, shape=(N, K // 4))
+    _want(deq, "deq", torch.float32, numel=M)
+    _want(w_scale, "w_scale", torch.float32, numel=1)
+    _want(y, "y", torch.float32, shape=(M, N), optional=True)
     _dev(codes, deq, Wq, w_scale, y)
-    M, N = codes.shape[0], Wq.shape[0]
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=codes.device)
     _check(lib().hbl_gemm_dequant(_ptr(codes), _ptr(deq), _ptr(Wq), _ptr(w_scale), M, K, N, int(abits), _ptr(y),
@@ -178,9 +217,15 @@ def forward(x, Wq, w_scale, abits: int, use_hadamard: bool, norm: bool = False, 
     """The whole (H-)BitLinear forward: x [M, K] -> y fp32 [M, N]."""
     import torch
 
+    M, K = _rows(x, "x")
+    _xdtype(x)
+    N = _rows(Wq, "Wq")[0]
+    _want(Wq, "Wq", torch.uint8, shape=(N, K // 4))
+    _want(w_scale, "w_scale", torch.float32, numel=1)
+    _want(gamma, "gamma", torch.float32, numel=K, optional=True)
+    _want(y, "y", torch.float32, shape=(M, N), optional=True)
+    _want(ws, "ws", torch.uint8, optional=True)
     _dev(x, Wq, w_scale, gamma, y, ws)
-    M, K = x.shape
-    N = Wq.shape[0]
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=x.device)
     if ws is None:
@@ -194,6 +239,9 @@ def forward(x, Wq, w_scale, abits: int, use_hadamard: bool, norm: bool = False, 
 def swiglu(g, u, h=None):
     import torch
 
+    _want(g, "g", torch.float32)
+    _want(u, "u", torch.float32, numel=g.numel())
+    _want(h, "h", torch.float32, numel=g.numel(), optional=True)
     _dev(g, u, h)
     if h is None:
         h = torch.empty_like(g)
@@ -207,8 +255,10 @@ def interleave_gate_up(Wq_gate, Wq_up, K: int):
     """Two packed weights [F, K/4] -> Wgu [2F, K/4], interleaved in blocks of 32 rows."""
     import torch
 
+    F = _rows(Wq_gate, "Wq_gate")[0]
+    _want(Wq_gate, "Wq_gate", torch.uint8, shape=(F, K // 4))
+    _want(Wq_up, "Wq_up", torch.uint8, shape=(F, K // 4))
     _dev(Wq_gate, Wq_up)
-    F = Wq_gate.shape[0]
     Wgu = torch.empty((2 * F, K // 4), dtype=torch.uint8, device=Wq_gate.device)
     _check(lib().hbl_interleave_gate_up(_ptr(Wq_gate), _ptr(Wq_up), F, K, _ptr(Wgu), _stream()))
     return Wgu
@@ -228,8 +278,14 @@ def gate_up_swiglu(codes, deq, Wgu, scale_gate, scale_up, K: int, abits: int, h_
     """h [M, F] = silu(g) * u for the shared codes/deq and interleaved gate/up weights."""
     import torch
 
+    M, F = _rows(codes, "codes")[0], _rows(Wgu, "Wgu")[0] // 2
+    _want(codes, "codes", torch.uint8, shape=(M, K * abits // 8))
+    _want(Wgu, "Wgu", torch.uint8, shape=(2 * F, K // 4))
+    _want(deq, "deq", torch.float32, numel=M)
+    _want(scale_gate, "scale_gate", torch.float32, numel=1)
+    _want(scale_up, "scale_up", torch.float32, numel=1)
+    _want(h, "h", shape=(M, F), optional=True)
     _dev(codes, deq, Wgu, scale_gate, scale_up, h)
-    M, F = codes.shape[0], Wgu.shape[0] // 2
     if h is None:
         h = torch.empty((M, F), dtype=h_dtype or torch.float32, device=codes.device)
     _check(lib().hbl_gate_up_swiglu(_ptr(codes), _ptr(deq), _ptr(Wgu), _ptr(scale_gate), _ptr(scale_up), M, K, F,
@@ -249,9 +305,18 @@ def ffn_forward(x, Wgu, scale_gate, scale_up, Wq_down, scale_down, abits: int = 
     """The FFN block x [M, D] -> y [M, D] fp32 (RMSNorm, gate/up, SwiGLU, H-BitLinear down)."""
     import torch
 
+    M, D = _rows(x, "x")
+    _xdtype(x)
+    F = _rows(Wgu, "Wgu")[0] // 2
+    _want(Wgu, "Wgu", torch.uint8, shape=(2 * F, D // 4))
+    _want(Wq_down, "Wq_down", torch.uint8, shape=(D, F // 4))
+    for name, t in (("scale_gate", scale_gate), ("scale_up", scale_up), ("scale_down", scale_down)):
+        _want(t, name, torch.float32, numel=1)
+    _want(gamma_in, "gamma_in", torch.float32, numel=D, optional=True)
+    _want(gamma_down, "gamma_down", torch.float32, numel=F, optional=True)
+    _want(y, "y", torch.float32, shape=(M, D), optional=True)
+    _want(ws, "ws", torch.uint8, optional=True)
     _dev(x, Wgu, scale_gate, scale_up, Wq_down, scale_down, gamma_in, gamma_down, y, ws)
-    M, D = x.shape
-    F = Wgu.shape[0] // 2
     h_dtype = h_dtype or torch.float32
     if y is None:
         y = torch.empty((M, D), dtype=torch.float32, device=x.device)
@@ -269,8 +334,9 @@ def quantize_qkv(x, bits: int):
     """x [rows, d] (post-RoPE head vectors, bf16/fp32) -> (codes uint8 [rows, d*bits/8], gamma fp32 [rows])."""
     import torch
 
+    rows, d = _rows(x, "x")
+    _xdtype(x)
     _dev(x)
-    rows, d = x.shape
     codes = torch.empty((rows, d * bits // 8), dtype=torch.uint8, device=x.device)
     gamma = torch.empty(rows, dtype=torch.float32, device=x.device)
     _check(lib().hbl_quantize_qkv(_ptr(x), _xdtype(x), rows, d, int(bits), _ptr(codes), _ptr(gamma), _stream()))
@@ -280,8 +346,10 @@ def quantize_qkv(x, bits: int):
 def dequantize_qkv(codes, gamma, d: int, bits: int):
     import torch
 
+    rows = _rows(codes, "codes")[0]
+    _want(codes, "codes", torch.uint8, shape=(rows, d * bits // 8))
+    _want(gamma, "gamma", torch.float32, numel=rows)
     _dev(codes, gamma)
-    rows = codes.shape[0]
     out = torch.empty((rows, d), dtype=torch.float32, device=codes.device)
     _check(lib().hbl_dequantize_qkv(_ptr(codes), _ptr(gamma), rows, d, int(bits), _ptr(out), _stream()))
     return out
@@ -293,8 +361,9 @@ def weights_to_fp4(Wq, K: int):
     """2-bit Wq [N, K/4] -> FP4 Wq4 [N, K/2] (the weight scale is unchanged)."""
     import torch
 
+    N = _rows(Wq, "Wq")[0]
+    _want(Wq, "Wq", torch.uint8, shape=(N, K // 4))
     _dev(Wq)
-    N = Wq.shape[0]
     Wq4 = torch.empty((N, K // 2), dtype=torch.uint8, device=Wq.device)
     _check(lib().hbl_weights_to_fp4(_ptr(Wq), N, K, _ptr(Wq4), _stream()))
     return Wq4
@@ -304,8 +373,10 @@ def quantize_activations_fp6(x, use_hadamard: bool, norm: bool = False, gamma=No
     """x [M, K] -> (codes6 uint8 [M, 3K/4], deq fp32 [M]); the INT4 codes stored as FP6."""
     import torch
 
+    M, K = _rows(x, "x")
+    _xdtype(x)
+    _want(gamma, "gamma", torch.float32, numel=K, optional=True)
     _dev(x, gamma)
-    M, K = x.shape
     codes = torch.empty((M, K // 4 * 3), dtype=torch.uint8, device=x.device)
     deq = torch.empty(M, dtype=torch.float32, device=x.device)
     _check(lib().hbl_quantize_activations_fp6(_ptr(x), _xdtype(x), M, K, HBL_NORM_RMS if norm else HBL_NORM_NONE,
@@ -317,8 +388,10 @@ def quantize_activations_fp6(x, use_hadamard: bool, norm: bool = False, gamma=No
 def gemm_fp6fp4_s32(codes6, Wq4, K: int):
     import torch
 
+    M, N = _rows(codes6, "codes6")[0], _rows(Wq4, "Wq4")[0]
+    _want(codes6, "codes6", torch.uint8, shape=(M, K // 4 * 3))
+    _want(Wq4, "Wq4", torch.uint8, shape=(N, K // 2))
     _dev(codes6, Wq4)
-    M, N = codes6.shape[0], Wq4.shape[0]
     acc = torch.empty((M, N), dtype=torch.int32, device=codes6.device)
     _check(lib().hbl_gemm_fp6fp4_s32(_ptr(codes6), _ptr(Wq4), M, K, N, _ptr(acc), _stream()))
     return acc
@@ -327,8 +400,13 @@ def gemm_fp6fp4_s32(codes6, Wq4, K: int):
 def gemm_fp6fp4_dequant(codes6, deq, Wq4, w_scale, K: int, y=None):
     import torch
 
+    M, N = _rows(codes6, "codes6")[0], _rows(Wq4, "Wq4")[0]
+    _want(codes6, "codes6", torch.uint8, shape=(M, K // 4 * 3))
+    _want(Wq4, "Wq4", torch.uint8, shape=(N, K // 2))
+    _want(deq, "deq", torch.float32, numel=M)
+    _want(w_scale, "w_scale", torch.float32, numel=1)
+    _want(y, "y", torch.float32, shape=(M, N), optional=True)
     _dev(codes6, deq, Wq4, w_scale, y)
-    M, N = codes6.shape[0], Wq4.shape[0]
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=codes6.device)
     _check(lib().hbl_gemm_fp6fp4_dequant(_ptr(codes6), _ptr(deq), _ptr(Wq4), _ptr(w_scale), M, K, N, _ptr(y),
@@ -340,9 +418,15 @@ def forward_fp6fp4(x, Wq4, w_scale, use_hadamard: bool, norm: bool = False, gamm
                    y=None, ws=None):
     import torch
 
+    M, K = _rows(x, "x")
+    _xdtype(x)
+    N = _rows(Wq4, "Wq4")[0]
+    _want(Wq4, "Wq4", torch.uint8, shape=(N, K // 2))
+    _want(w_scale, "w_scale", torch.float32, numel=1)
+    _want(gamma, "gamma", torch.float32, numel=K, optional=True)
+    _want(y, "y", torch.float32, shape=(M, N), optional=True)
+    _want(ws, "ws", torch.uint8, optional=True)
     _dev(x, Wq4, w_scale, gamma, y, ws)
-    M, K = x.shape
-    N = Wq4.shape[0]
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=x.device)
     if ws is None:

@@ -326,6 +326,9 @@ __device__ __forceinline__ void actquant_rows(
   __shared__ float lds[NP > 1 ? R * ROWF : 1];
   __shared__ float redf[NW];
   __shared__ double redd[NW];
+  // The absmean sum has slots of its own: without the transform no barrier separates it from
+  // the sum of squares, whose slots slower waves of the row may still be reading.
+  __shared__ double redd2[ABITS == 5 ? NW : 1];
 
   const int tid = threadIdx.x;
   const int rl = tid / T;
@@ -396,7 +399,7 @@ __device__ __forceinline__ void actquant_rows(
       double sa = 0.0;
 #pragma unroll
       for (int j = 0; j < 64; ++j) sa += (double)fabsf(v[j]);
-      amax = (float)(row_sum<T>(sa, redd) / (double)K);  // the absmean statistic b
+      amax = (float)(row_sum<T>(sa, redd2) / (double)K);  // the absmean statistic b
     } else {
 #pragma unroll
       for (int j = 0; j < 64; ++j) amax = fmaxf(amax, fabsf(v[j]));

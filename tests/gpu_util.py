@@ -47,3 +47,20 @@ def assert_close_ulps(got, want, ulps: int = 4, what: str = ""):
     tol = np.abs(want) * (ulps * 2.0 ** -23) + 1e-37
     bad = np.abs(got.astype(np.float64) - want.astype(np.float64)) > tol
     assert not bad.any(), f"{what}: {int(bad.sum())} of {bad.size} values differ by more than {ulps} ulp"
+
+
+def code_diffs(orc, got_packed, q_o, K: int, abits: int):
+    """Unpacks GPU codes and returns |GPU - oracle| per code (int32 array)."""
+    got = orc.unpack_codes(np.ascontiguousarray(got_packed), K, abits).astype(np.int32)
+    return np.abs(got - np.asarray(q_o, np.int32))
+
+
+def assert_code_bar(orc, got_packed, q_o, K: int, abits: int, what: str = "", frac: float = 1e-4):
+    """The method's bar for codes decided in another summation order: at most `frac` of the
+    codes differ from the oracle's, each by one step."""
+    d = code_diffs(orc, got_packed, q_o, K, abits)
+    n = int((d != 0).sum())
+    note(f"{what}: {n} of {d.size} codes differ ({n / max(d.size, 1):.2e}), max |diff| {int(d.max()) if d.size else 0}")
+    assert d.size == 0 or d.max() <= 1, f"{what}: codes differ by {d.max()}"
+    assert n <= frac * d.size, f"{what}: {n} of {d.size} codes differ"
+    return n / max(d.size, 1)

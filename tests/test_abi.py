@@ -302,3 +302,4 @@ def test_probe_library_exports_its_entry_point():
     f = lib.hbl_probe_mfma_ceiling
     f.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     assert f(None, 1, 1, FAKE, S) == 1 and f(FAKE, 0, 1, FAKE, S) == 1   # rejected before any HIP call
+

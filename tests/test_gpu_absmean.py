@@ -34,16 +34,19 @@ def test_absmean_hadamard(orc, L):
     assert_close_ulps(to_host(deq), deq_o, 2, "deq")
 
 
-@pytest.mark.parametrize("K", [64, 576, 4096, 20480])
-@pytest.mark.parametrize("fmt", ["bf16", "fp32-gamma"])
+# K = 8192 and 16384 run the persistent row kernel with rows spread over two and four waves,
+# where the absmean and sum-of-squares reductions each need their own slots.
+@pytest.mark.parametrize("K", [64, 576, 4096, 8192, 16384, 20480])
+@pytest.mark.parametrize("fmt", ["bf16", "bf16-gamma", "fp32-gamma"])
 def test_absmean_plain(orc, K, fmt):
     note("absmean plain", K, fmt)
     M = 130
     x = inputs.make_activations("normal", M, K, outlier_frac=0.02, outlier_scale=40.0, seed=K)
     gamma = None
     if fmt != "bf16":
-        x = inputs.bf16_bits_to_f32(x) * np.float32(0.5)
         gamma = np.random.default_rng(K).uniform(0.5, 2.0, K).astype(np.float32)
+    if fmt == "fp32-gamma":
+        x = inputs.bf16_bits_to_f32(x) * np.float32(0.5)
     codes, deq = B.quantize_activations(to_dev(x), 4, False, norm=True, gamma=None if gamma is None else to_dev(gamma),
                                         stat=B.HBL_STAT_ABSMEAN)
     q_o, deq_o, _ = orc.quantize_activations(x, 4, False, norm=True, gamma=gamma, stat=1)

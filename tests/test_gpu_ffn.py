@@ -2,16 +2,26 @@
 
 The fused kernel computes g and u exactly as hbl_gemm_dequant does and applies the same
 device SwiGLU as hbl_swiglu, so its h must equal the unfused GPU sequence bit for bit
-(fp32), and the bf16 h must equal torch's round-to-nearest-even cast of that fp32 h.  Against
-the oracle: h within 8 ulp of the fp64-evaluated SwiGLU of the oracle's g and u, and the
-block output within the method's bar (relative Frobenius error <= 1e-3).
+(fp32), and the bf16 h must equal torch's round-to-nearest-even cast of that fp32 h.
+
+Against the oracle:
+  - h is within 8 ulp of the fp64-evaluated SwiGLU of the oracle's g and u (fp32), or one
+    bf16 step apart on fewer than 1e-3 of its elements (bf16);
+  - the down projection run by the oracle on the GPU's own h meets the H-BitLinear bar
+    (relative Frobenius error <= 1e-3, within 4 ulp apart from flipped codes);
+  - the whole block meets the method's code bar: at most 1e-4 of the down projection's
+    INT4/INT8 codes differ from the oracle block's codes, each by one step.
+The block output is not held to relative Frobenius 1e-3: one code of a row that moves by one
+step moves that row's output by about 1/sqrt(F * E[q^2]) of its norm (about 0.4 % for INT4
+at F = 16384), so a single flipped code exceeds 1e-3.  The output bar asserted is the one
+the code bar implies, 2 * sqrt(f / E[q^2]) for a measured fraction f of flipped codes.
 """
 import numpy as np
 import pytest
 
 from bit_quantized_gemm_bitlinear_amd import binding as B
 from bit_quantized_gemm_bitlinear_amd import inputs
-from tests.gpu_util import assert_close_ulps, note, rel_fro, to_dev, to_host, torch_mod
+from tests.gpu_util import assert_close_ulps, assert_code_bar, note, rel_fro, to_dev, to_host, torch_mod
 
 pytestmark = pytest.mark.gpu
 
@@ -109,7 +119,12 @@ def _block(orc, M, D, F, abits, h_bf16, x=None, sample=None):
                                intermediates=True)
     h_s = np.ascontiguousarray(h[rows])
     y_down = orc.forward(h_s, Td, ad, abits, True, norm=True)
-    return dict(y=y[rows], h=h_s, y_o=y_o, h_o=h_o, y_down=y_down, ctx=(x, qg, sg, qu, su, qd, sd, Wgu, ht))
+    # the down projection's codes, left in the workspace, and the oracle block's codes
+    off2 = off + _r256(M * F * hb)
+    codes2 = to_host(ws[off2:off2 + M * F * abits // 8]).reshape(M, F * abits // 8)[rows]
+    q_o = orc.quantize_activations(h_o, abits, True, norm=True)[0]
+    return dict(y=y[rows], h=h_s, y_o=y_o, h_o=h_o, y_down=y_down, codes2=codes2, q_o=q_o, F=F, abits=abits,
+                ctx=(x, qg, sg, qu, su, qd, sd, Wgu, ht))
 
 
 def _ordered_bf16(b):
@@ -128,9 +143,13 @@ def _check_block(r, h_bf16):
     # down projection on the GPU's own h: the H-BitLinear bar
     assert rel_fro(r["y"], r["y_down"]) <= 1e-3
     assert_close_ulps(r["y"], r["y_down"], 4, "down projection")
-    # whole block: a one-step difference in h can move an INT4 code of the down projection
-    # by one, which moves that row by about 1/sqrt(F * E[q^2]) (~0.4% at F = 16384)
-    assert rel_fro(r["y"], r["y_o"]) <= 1e-2
+    # whole block: the code bar on the down projection's codes, then the output bar it implies
+    f = assert_code_bar(_orc(), r["codes2"], r["q_o"], r["F"], r["abits"], "block codes")
+    eq2 = float(np.mean(np.asarray(r["q_o"], np.float64) ** 2))
+    err = rel_fro(r["y"], r["y_o"])
+    bound = 2.0 * np.sqrt(f / eq2) + 1e-4
+    note(f"block: relative Frobenius error {err:.3e} (bound from the code bar {bound:.3e}, E[q^2] {eq2:.2f})")
+    assert err <= bound
 
 
 @pytest.mark.parametrize("h_bf16", [True, False])
@@ -154,11 +173,21 @@ def test_ffn_forward_equals_separate_calls(orc):
     np.testing.assert_array_equal(r["y"].view(np.int32), y2.view(np.int32))
 
 
-def test_ffn_full_size_sampled_rows(orc):
-    """The 7B-like block at its full size (M=8192, D=4096, F=16384), bf16 h, 24 sampled rows."""
+@pytest.mark.parametrize("h_bf16", [True, False])
+def test_ffn_full_size_stratified_rows(orc, h_bf16):
+    """The 7B-like block at its full size (M=8192, D=4096, F=16384) in the launch bench.py
+    times; the oracle checks 4 seeded rows of every 128-row band (every row tile of both
+    GEMMs), 258 rows with the first and the last."""
     wl = inputs.WORKLOADS["ffn_7b"]
     M, D, F = wl.M, wl.extra["hidden"], wl.extra["ffn"]
-    note("ffn full size", M, D, F)
+    note("ffn full size", M, D, F, "bf16 h" if h_bf16 else "fp32 h")
     rng = np.random.default_rng(99)
-    sample = np.unique(np.concatenate([rng.choice(M, 22, replace=False), [0, M - 1]]))
-    _check_block(_block(orc, M, D, F, 4, True, x=wl.activations(), sample=sample), True)
+    bands = [b * 128 + rng.choice(128, 4, replace=False) for b in range(M // 128)]
+    sample = np.unique(np.concatenate(bands + [np.array([0, M - 1])]))
+    _check_block(_block(orc, M, D, F, 4, h_bf16, x=wl.activations(), sample=sample), h_bf16)
+
+
+def _orc():
+    import oracle
+
+    return oracle
