@@ -43,8 +43,17 @@ def common_flags() -> list[str]:
             "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 
+# Per-file extra flags.  The activation kernels read the results of their bf16 matrix
+# products with VALU instructions: the VGPR form of the MFMAs writes them straight to VGPRs
+# instead of AGPRs (saves one v_accvgpr_read per value).
+EXTRA_FLAGS = {
+    "k_actquant_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "k_actquant.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def _compile(src: str, obj: str) -> tuple[str, int, str]:
-    cmd = [hipcc(), "-x", "hip", "-c", src, "-o", obj] + common_flags()
+    cmd = [hipcc(), "-x", "hip", "-c", src, "-o", obj] + common_flags() + EXTRA_FLAGS.get(os.path.basename(src), [])
     p = subprocess.run(cmd, capture_output=True, text=True)
     # The host pass does not know the packed-fp32 target feature; that warning is harmless.
     err = "\n".join(l for l in (p.stderr or "").splitlines() if "packed-fp32-ops" not in l)

@@ -17,6 +17,13 @@ hipError_t launch_wquant(const float* W, int64_t N, int64_t K, uint8_t* Wq, floa
 hipError_t launch_actquant(const void* x, int xt, int64_t M, int64_t K, int norm, const float* gamma,
                            float eps, int abits, int use_h, uint8_t* codes, float* deq, hipStream_t s);
 
+// bf16 rows with unit gamma and K = 2^10 .. 2^14 under the transform take the activation
+// kernel whose first five transform stages run on the matrix cores (k_actquant_mfma.hip);
+// launch_actquant dispatches to it.  abits as launch_actquant.
+bool actquant_mfma_ok(int xt, int64_t K, const float* gamma, int norm, int use_h);
+hipError_t launch_actquant_mfma(const void* x, int64_t M, int64_t K, int norm, float eps, int abits, uint8_t* codes,
+                                float* deq, hipStream_t s);
+
 // The whole H-BitLinear forward for a few token rows in one kernel (k_actquant.hip): applies
 // when decode_fused_ok(M, K, abits, use_h); writes codes/deq (workspace) and y like the
 // two-kernel path, bit for bit.

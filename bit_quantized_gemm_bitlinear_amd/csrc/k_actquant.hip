@@ -25,6 +25,8 @@
 // change under a positive per-row scale, so both are folded into deq.
 #include <cmath>
 
+#include "actquant_mfma.h"
+#include "actquant_store.h"
 #include "hbl_device.h"
 #include "hbl_internal.h"
 
@@ -114,121 +116,6 @@ __device__ __forceinline__ double row_sum(double v, double* red) {
 #pragma unroll
     for (int i = 1; i < T / 64; ++i) s += red[w0 + i];
     return s;
-  }
-}
-
-// ABITS: 4 = INT4 codes packed as nibbles, 8 = INT8 codes, 6 = INT4 codes (Qb = 7) stored as
-// FP6 E2M3 (6 bits each, code k at bits [6k, 6k+6) of the row's little-endian bit string),
-// 5 = INT4 codes packed as nibbles with the absmean statistic instead of absmax:
-// b = mean|z| (fp64 sum), s = fl32(1/b), q = clamp(rint(z*s), -8, 7), deq = b*r*hK.
-template <int ABITS>
-struct QB {
-  static constexpr float value = ABITS == 8 ? 127.0f : 7.0f;
-};
-
-template <int ABITS>
-constexpr int row_bytes(int K) { return (ABITS == 4 || ABITS == 5) ? K / 2 : (ABITS == 8 ? K : K * 6 / 8); }
-
-typedef float v16f_t __attribute__((ext_vector_type(16)));
-
-// 2 to 32 integer-valued floats (|q| <= 7) -> FP6 E2M3, packed 6 bits each in element order.
-// The hardware conversion interleaves its two 16-wide operands (element 2i from the first,
-// 2i+1 from the second); the scale 1.0 leaves values unscaled.  Exact for these integers.
-template <int NV>
-__device__ __forceinline__ void fp6_pack(const float* q, uint32_t (&w)[6]) {
-  v16f_t ev, od;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    ev[i] = 2 * i < NV ? q[2 * i] : 0.0f;
-    od[i] = 2 * i + 1 < NV ? q[2 * i + 1] : 0.0f;
-  }
-  const auto r = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, 1.0f);
-#pragma unroll
-  for (int i = 0; i < 6; ++i) w[i] = (uint32_t)r[i];
-}
-
-// Store NWORDS packed 32-bit words to dst (aligned to 4 * min(NWORDS, 4) bytes).
-template <int NWORDS>
-__device__ __forceinline__ void store_words(uint8_t* dst, const uint32_t* w) {
-  if constexpr (NWORDS >= 4) {
-#pragma unroll
-    for (int d = 0; d < NWORDS; d += 4)
-      *reinterpret_cast<uint4*>(dst + 4 * d) = make_uint4(w[d], w[d + 1], w[d + 2], w[d + 3]);
-  } else if constexpr (NWORDS == 2) {
-    *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
-  } else {
-    *reinterpret_cast<uint32_t*>(dst) = w[0];
-  }
-}
-
-// Round-half-even to an integer through the fp32 adder: for |v| <= 2^21, v + (1.5*2^23 + c)
-// rounds to the integer rint(v) + c (spacing 1 in [2^23, 2^24), ties to even; c even keeps
-// the parity), whose low mantissa bits are then rint(v) + c in two's complement.
-__device__ __forceinline__ uint32_t rne_bits(float v, float magic) { return __float_as_uint(v + magic); }
-
-// Quantise a run of RL consecutive row elements v[0 .. RL) (scale s) starting at row
-// element k0 and store its packed bytes.
-//  INT4: offset magic +8 gives low nibble q+8 in [1,15] with zero bits above it, so a pair
-//        (lo, hi) becomes one byte with a single shift-or; four bytes are gathered with
-//        v_perm and the offset is removed with one xor (q+8 ^ 8 = q mod 16).
-//  INT8: the low byte of the rounded value is q mod 256; four are gathered with v_perm.
-template <int ABITS, int RL>
-__device__ __forceinline__ void store_run(const float* v, float s, uint8_t* __restrict__ crow, int k0) {
-  constexpr float MAGIC = 12582912.0f;  // 1.5 * 2^23
-  if constexpr (ABITS == 6) {
-    // rint first (the FP6 grid is finer than the integers below 4), then the exact conversion.
-    uint8_t* dst = crow + (k0 / 8) * 6;
-#pragma unroll
-    for (int c = 0; c < RL; c += 32) {
-      constexpr int NV = RL < 32 ? RL : 32;
-      float q[NV];
-#pragma unroll
-      for (int i = 0; i < NV; ++i) q[i] = __builtin_rintf(v[c + i] * s) + 0.0f;  // +0.0f: -0 -> +0 (code 0x00)
-      uint32_t w[6];
-      fp6_pack<NV>(q, w);
-      if constexpr (NV == 32) {
-#pragma unroll
-        for (int i = 0; i < 3; ++i) reinterpret_cast<uint2*>(dst + 24 * (c / 32))[i] = make_uint2(w[2 * i], w[2 * i + 1]);
-      } else if constexpr (NV == 16) {
-#pragma unroll
-        for (int i = 0; i < 3; ++i) reinterpret_cast<uint32_t*>(dst)[i] = w[i];
-      } else {  // 8 codes = 48 bits, 2-byte aligned
-        uint16_t* d16 = reinterpret_cast<uint16_t*>(dst);
-        d16[0] = (uint16_t)(w[0] & 0xffffu);
-        d16[1] = (uint16_t)(w[0] >> 16);
-        d16[2] = (uint16_t)(w[1] & 0xffffu);
-      }
-    }
-  } else if constexpr (ABITS == 4 || ABITS == 5) {
-    // absmean codes can exceed the INT4 range: clamp before rounding (same as after, the
-    // bounds being integers)
-    auto sc = [&](float z) { return ABITS == 5 ? fminf(fmaxf(z * s, -8.0f), 7.0f) : z * s; };
-    uint32_t w[RL / 8];
-#pragma unroll
-    for (int d = 0; d < RL / 8; ++d) {
-      uint32_t b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t lo = rne_bits(sc(v[8 * d + i]), MAGIC + 8.0f);
-        const uint32_t hi = rne_bits(sc(v[8 * d + i + 4]), MAGIC + 8.0f);
-        b[i] = (hi << 4) | lo;  // byte 0 = (hi+8) << 4 | (lo+8); higher bytes unused
-      }
-      const uint32_t b01 = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u);
-      const uint32_t b23 = __builtin_amdgcn_perm(b[3], b[2], 0x04000c0cu);
-      w[d] = (b01 | b23) ^ 0x88888888u;
-    }
-    store_words<RL / 8>(crow + k0 / 2, w);
-  } else {
-    uint32_t w[RL / 4];
-#pragma unroll
-    for (int d = 0; d < RL / 4; ++d) {
-      const uint32_t q0 = rne_bits(v[4 * d + 0] * s, MAGIC), q1 = rne_bits(v[4 * d + 1] * s, MAGIC);
-      const uint32_t q2 = rne_bits(v[4 * d + 2] * s, MAGIC), q3 = rne_bits(v[4 * d + 3] * s, MAGIC);
-      const uint32_t lo = __builtin_amdgcn_perm(q1, q0, 0x0c0c0400u);
-      const uint32_t hi = __builtin_amdgcn_perm(q3, q2, 0x04000c0cu);
-      w[d] = lo | hi;
-    }
-    store_words<RL / 4>(crow + k0, w);
   }
 }
 
@@ -481,25 +368,80 @@ __global__ __launch_bounds__(block_threads<L>()) void k_decode_h(
   constexpr int G = K / (NW * 256);   // 256-deep weight groups per wave
   constexpr float Qb = QB<ABITS>::value;
   static_assert(NP == 3 && G >= 1, "the fused decode kernel covers K = 2^12 .. 2^15");
-  __shared__ float lds[R * ROWF];
+  // bf16 rows with unit gamma take the matrix-core transform of the activation kernel for such
+  // rows (actquant_mfma.h), so that codes and deq are the ones that kernel writes
+  constexpr bool HM = XT == 1 && NM != 2 && L <= 14;
+  constexpr int LDSF = HM && HM_LDS_FLOATS > R * ROWF ? HM_LDS_FLOATS : R * ROWF;
+  __shared__ __attribute__((aligned(16))) float lds[LDSF];
   __shared__ __attribute__((aligned(16))) int8_t cl[MMAX * CST];
   __shared__ float dl[MMAX];
   __shared__ float redf[NW];
   __shared__ double redd[NW];
+  __shared__ double redd2[NW];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int rl = tid / T, t = tid % T;
   const int gq = lane >> 4, rq = lane & 15;   // MFMA lane coordinates
   const int n0 = blockIdx.x * 16;
+  const uint8_t* brow = Wq + (int64_t)min(n0 + rq, N - 1) * (K / 4) + 16 * gq;
+  uint4 wb[G];
 
+  if constexpr (HM) {
+    static_assert(HM_SLAB / K == R, "one slab holds the rows of one group");
+    // 1) The slab of rows, then the block's weights (loads complete in issue order).
+    uint4 raw[8];
+    hm_load<L>(raw, static_cast<const uint16_t*>(x), M, 0, wave, lane);
+    __builtin_amdgcn_sched_barrier(0);  // keep the issue order
+#pragma unroll
+    for (int u = 0; u < G; ++u) wb[u] = *reinterpret_cast<const uint4*>(brow + 64 * (wave * G + u));
+    // 2) Transform and quantise; int8 codes to LDS, and from block 0 the packed codes and deq.
+    using P = HmPost<L>;
+    constexpr int RL = P::RL;
+    float v[64];
+    HmStats st;
+    hm_transform<L, ABITS, NM>(raw, hm_hadamard_b(lane, 0), hm_hadamard_b(lane, 1), lds, redf, redd, redd2, wave,
+                               lane, v, st, [] {});
+    const int E0 = P::thread_E(wave, lane);
+    const int row = E0 >> L;
+    // RMS factor 1/sqrt(mean(x^2) + eps): the mean in fp64, the reciprocal square root by
+    // v_rsq_f32 (about one ulp; the sum of squares is already an fp32 sum per lane)
+    const float r = NM != 0 ? __builtin_amdgcn_rsqf((float)(st.ss / (double)K + (double)eps)) : 1.0f;
+    const bool zero = st.amax < 0x1p-120f;
+    const float s = zero ? 0.0f : Qb / st.amax;
+    if (row < M) {
+      int8_t* crow = cl + row * CST;
+#pragma unroll
+      for (int gi = 0; gi < 64 / RL; ++gi) {
+        const int k0 = (E0 + P::reg_E(gi * RL)) & (K - 1);
+#pragma unroll
+        for (int d = 0; d < RL / 4; ++d) {
+          const float* q = v + gi * RL + 4 * d;
+          const uint32_t q0 = rne_bits(q[0] * s, 12582912.0f), q1 = rne_bits(q[1] * s, 12582912.0f);
+          const uint32_t q2 = rne_bits(q[2] * s, 12582912.0f), q3 = rne_bits(q[3] * s, 12582912.0f);
+          const uint32_t lo = __builtin_amdgcn_perm(q1, q0, 0x0c0c0400u);
+          const uint32_t hi = __builtin_amdgcn_perm(q3, q2, 0x04000c0cu);
+          *reinterpret_cast<uint32_t*>(crow + k0 + 4 * d) = lo | hi;
+        }
+      }
+      const float dq = zero ? 0.0f : __fmul_rn(__fmul_rn(st.amax / Qb, r), hK);
+      const bool first = (E0 & (K - 1)) == 0;
+      if (first) dl[row] = dq;
+      if (blockIdx.x == 0) {
+        uint8_t* grow = codes + (int64_t)row * row_bytes<ABITS>(K);
+#pragma unroll
+        for (int gi = 0; gi < 64 / RL; ++gi)
+          store_run<ABITS, RL>(v + gi * RL, s, grow, (E0 + P::reg_E(gi * RL)) & (K - 1));
+        if (first) deq[row] = dq;
+      }
+    }
+    __syncthreads();  // codes and deq in LDS before the product
+  } else {
   // 1) The first activation rows, then the block's weights (lane (gq, rq) of wave w holds
   //    chunk 4 (w G + u) + gq of row n0 + rq).  Loads complete in issue order, so the rows
   //    go first: the transform can start while the weights are still streaming in.
   RowChunk<XT> cur;
   load_chunk<XT>(cur, x, (int64_t)min(rl, M - 1) * K + 64 * t);
   __builtin_amdgcn_sched_barrier(0);  // keep the issue order
-  const uint8_t* brow = Wq + (int64_t)min(n0 + rq, N - 1) * (K / 4) + 16 * gq;
-  uint4 wb[G];
 #pragma unroll
   for (int u = 0; u < G; ++u) wb[u] = *reinterpret_cast<const uint4*>(brow + 64 * (wave * G + u));
 
@@ -586,6 +528,7 @@ __global__ __launch_bounds__(block_threads<L>()) void k_decode_h(
   for (int grp = 1; grp < ngroups; ++grp) {
     load_chunk<XT>(cur, x, (int64_t)min(grp * R + rl, M - 1) * K + 64 * t);
     process_group(grp);
+  }
   }
 
   // 3) The product: wave w covers groups [w G, w G + G) of K; step t of group C pairs k-block
@@ -886,6 +829,8 @@ hipError_t launch_decode_fused(const void* x, int xt, int64_t M, int64_t K, int 
 hipError_t launch_actquant(const void* x, int xt, int64_t M, int64_t K, int norm, const float* gamma, float eps,
                            int abits, int use_h, uint8_t* codes, float* deq, hipStream_t s) {
   if (M == 0) return hipSuccess;
+  if (actquant_mfma_ok(xt, K, gamma, norm, use_h))
+    return launch_actquant_mfma(x, M, K, norm, eps, abits, codes, deq, s);
   if (use_h) {
     int L = 0;
     while ((int64_t(1) << L) < K) ++L;

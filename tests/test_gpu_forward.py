@@ -2,10 +2,12 @@
 the CPU oracle on the five synthetic workloads.
 
 Bars: on the exact-arithmetic workload (integer activations, no norm) codes, int32
-accumulators and outputs are bit-identical.  On the Gaussian/outlier workloads the codes
-are bit-identical too (the GPU transform runs the same fp32 butterflies in the same order)
-and the outputs agree within 4 ulp (the RMS sum is reduced in another order); the
-acceptance bar of the method, relative Frobenius error <= 1e-3, is asserted as well.
+accumulators and outputs are bit-identical.  On the Gaussian/outlier workloads (bf16 rows,
+whose first five transform stages run on the matrix cores and are summed in another order)
+the codes meet the method's code bar (at most 1e-4 of them differ from the oracle's, each by
+one step), the outputs meet its bar (relative Frobenius error <= 1e-3) and are within 4 ulp
+on every row whose codes all match (plus the few ulp by which deq differs: its sum of squares
+is taken in fp32 and g = max|z| is summed in another order).
 Full-size cases run exactly the launch that bench.py times and compare every row with the
 oracle.
 """
@@ -14,7 +16,8 @@ import pytest
 
 from bit_quantized_gemm_bitlinear_amd import binding as B
 from bit_quantized_gemm_bitlinear_amd import inputs
-from tests.gpu_util import assert_close_ulps, note, rel_fro, to_dev, to_host, torch_mod
+from tests.gpu_util import (assert_close_ulps, assert_rows_close, check_codes, mfma_transform, note, rel_fro,
+                            to_dev, to_host, torch_mod)
 
 pytestmark = pytest.mark.gpu
 
@@ -36,28 +39,31 @@ def _layer(orc, wl, abits, M=None, sample=None, seed_w=inputs.SEED_W):
     # the codes written to the workspace by the same call
     ab = x.shape[0] * wl.K * abits // 8
     codes = to_host(ws[:ab]).reshape(x.shape[0], wl.K * abits // 8)[rows]
-    np.testing.assert_array_equal(codes, orc.pack_codes(q_o, abits))
-    return y[rows], y_o, acc_o, deq_o, (xd, Wq, scale, ws)
+    exact = not mfma_transform(x, wl.K, wl.use_hadamard)
+    rows_ok = check_codes(orc, codes, q_o, wl.K, abits, exact, f"{wl.name} a{abits} codes")
+    return y[rows], y_o, acc_o, deq_o, (xd, Wq, scale, ws, rows_ok, exact)
 
 
 def test_tiny_exact_bit_exact(orc):
     wl = inputs.WORKLOADS["tiny_exact"]
     note("forward tiny_exact")
-    y, y_o, acc_o, deq_o, (xd, Wq, scale, ws) = _layer(orc, wl, 4)
+    y, y_o, acc_o, deq_o, (xd, Wq, scale, ws, _, _) = _layer(orc, wl, 4)
     np.testing.assert_array_equal(y, y_o)
     codes_d, deq_d = B.quantize_activations(xd, 4, True)
     np.testing.assert_array_equal(to_host(deq_d), deq_o)
     np.testing.assert_array_equal(to_host(B.gemm_s32(codes_d, Wq, wl.K, 4)), acc_o)
 
 
-@pytest.mark.parametrize("name,abits,M", [("wo_1p3b", 8, 96), ("wo_1p3b", 4, 96), ("wdown_3b", 4, 40),
-                                          ("wdown_7b", 4, 24), ("wdown_7b", 8, 24)])
+# Enough rows that one flipped code does not dominate the relative Frobenius error: a flip
+# moves its row by about 1/sqrt(K E[q^2]) (1.2 % at K = 2048 with INT4), that is by
+# 1/sqrt(K E[q^2] M) of the whole output.
+@pytest.mark.parametrize("name,abits,M", [("wo_1p3b", 8, 512), ("wo_1p3b", 4, 512), ("wdown_3b", 4, 400),
+                                          ("wdown_7b", 4, 256), ("wdown_7b", 8, 256)])
 def test_workload_rows(orc, name, abits, M):
     wl = inputs.WORKLOADS[name]
     note("forward", name, abits, M)
-    y, y_o, _, _, _ = _layer(orc, wl, abits, M=M)
-    assert rel_fro(y, y_o) <= 1e-3
-    assert_close_ulps(y, y_o, 4, name)
+    y, y_o, _, _, ctx = _layer(orc, wl, abits, M=M)
+    assert_rows_close(y, y_o, ctx[-2], ctx[-1], name)
 
 
 def test_forward_deterministic(orc):
@@ -114,8 +120,5 @@ def test_full_size_all_rows(orc, name, abits):
     (so every output tile of the GEMM and every row group of the activation kernel)."""
     wl = inputs.WORKLOADS[name]
     note("full size", name, abits, wl.M, wl.K, wl.N)
-    y, y_o, _, _, _ = _layer(orc, wl, abits)
-    err = rel_fro(y, y_o)
-    note(f"full size {name} a{abits}: relative Frobenius error {err:.3e}")
-    assert err <= 1e-3
-    assert_close_ulps(y, y_o, 4, name)
+    y, y_o, _, _, ctx = _layer(orc, wl, abits)
+    assert_rows_close(y, y_o, ctx[-2], ctx[-1], f"full size {name} a{abits}")
