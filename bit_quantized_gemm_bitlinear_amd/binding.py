@@ -51,6 +51,7 @@ def lib() -> ctypes.CDLL:
             "hbl_forward": (I, [P, I, P, P, I64, I64, I64, I, I, I, P, F, P, P, SZ, P]),
             "hbl_swiglu": (I, [P, P, I64, P, P]),
             "hbl_forward_fused": (I, [I64, I64, I, I]),
+            "hbl_forward_noalloc": (I, [P, I, P, P, I64, I64, I64, I, I, I, P, F, P, P]),
             "hbl_quantize_activations_stat": (I, [P, I, I64, I64, I, P, F, I, I, I, P, P, P]),
             "hbl_forward_stat": (I, [P, I, P, P, I64, I64, I64, I, I, I, P, F, I, P, P, SZ, P]),
             "hbl_packed_weight_fp4_bytes": (SZ, [I64, I64]),
@@ -233,6 +234,28 @@ def forward(x, Wq, w_scale, abits: int, use_hadamard: bool, norm: bool = False, 
     _check(lib().hbl_forward_stat(_ptr(x), _xdtype(x), _ptr(Wq), _ptr(w_scale), M, K, N, int(abits),
                                   int(bool(use_hadamard)), HBL_NORM_RMS if norm else HBL_NORM_NONE, _ptr(gamma),
                                   float(eps), int(stat), _ptr(y), _ptr(ws), ws.numel(), _stream()))
+    return y
+
+
+def forward_noalloc(x, Wq, w_scale, abits: int, use_hadamard: bool, norm: bool = False, gamma=None,
+                    eps: float = 1e-5, y=None):
+    """hbl_forward_noalloc: the forward with its codes and deq in the library's static scratch
+    (no workspace; the library allocates nothing).  y is allocated here unless given."""
+    import torch
+
+    M, K = _rows(x, "x")
+    _xdtype(x)
+    N = _rows(Wq, "Wq")[0]
+    _want(Wq, "Wq", torch.uint8, shape=(N, K // 4))
+    _want(w_scale, "w_scale", torch.float32, numel=1)
+    _want(gamma, "gamma", torch.float32, numel=K, optional=True)
+    _want(y, "y", torch.float32, shape=(M, N), optional=True)
+    _dev(x, Wq, w_scale, gamma, y)
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    _check(lib().hbl_forward_noalloc(_ptr(x), _xdtype(x), _ptr(Wq), _ptr(w_scale), M, K, N, int(abits),
+                                     int(bool(use_hadamard)), HBL_NORM_RMS if norm else HBL_NORM_NONE, _ptr(gamma),
+                                     float(eps), _ptr(y), _stream()))
     return y
 
 

@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "hbl.h"
@@ -65,6 +66,59 @@ hbl_status check_act(const char* fn, hbl_dtype xt, hbl_norm norm, const float* g
     hbl_status st_ = (expr);       \
     if (st_ != HBL_OK) return st_; \
   } while (0)
+
+// The forward's launches once its arguments are validated: codes and deq of the M rows go
+// to ws (hbl_forward_workspace_bytes(M, K, abits) bytes, 256-byte aligned).
+hbl_status run_forward(const char* fn, const void* x, hbl_dtype xt, const uint8_t* Wq, const float* w_scale,
+                       int64_t M, int64_t K, int64_t N, int abits, int use_hadamard, hbl_norm norm,
+                       const float* gamma, float norm_eps, float* y, void* ws, void* stream) {
+  uint8_t* codes = static_cast<uint8_t*>(ws);
+  float* deq = reinterpret_cast<float*>(codes + round256((size_t)(M * K * abits / 8)));
+  hipStream_t s = (hipStream_t)stream;
+  const float* g = norm == HBL_NORM_RMS ? gamma : nullptr;
+  if (hbl::decode_fused_ok(M, K, abits, use_hadamard)) {  // a few rows: one fused kernel
+    hipError_t e = hbl::launch_decode_fused(x, (int)xt, M, K, (int)norm, g, norm_eps, abits, Wq, w_scale, N, codes,
+                                            deq, y, s);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return HBL_OK;
+  }
+  hipError_t e = hbl::launch_actquant(x, (int)xt, M, K, (int)norm, g, norm_eps, abits, use_hadamard, codes, deq, s);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  e = hbl::launch_gemm(codes, deq, Wq, w_scale, M, K, N, abits, nullptr, y, s);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  return HBL_OK;
+}
+
+}  // namespace
+
+// Scratch of hbl_forward_noalloc: the codes and deq of one call, in a device array that the
+// library owns (one copy per GPU, alive until the process ends).  Host code never passes the
+// array's name to a kernel: the name is a host-side stand-in, not a device address.  It uses
+// the address hipGetSymbolAddress returns for the current device, looked up once per device.
+static __device__ __align__(256) uint8_t scratch[HBL_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t scratch_of_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 }  // namespace
 
@@ -197,21 +251,34 @@ hbl_status hbl_forward(const void* x, hbl_dtype xt, const uint8_t* Wq, const flo
     if (ws == nullptr || ws_bytes < need)
       return fail(HBL_ERR_WORKSPACE, fn, "workspace missing or smaller than hbl_forward_workspace_bytes");
     HBL_TRY(check_ptr(fn, ws, "ws", 256));
-    uint8_t* codes = static_cast<uint8_t*>(ws);
-    float* deq = reinterpret_cast<float*>(codes + round256((size_t)(M * K * abits / 8)));
-    hipStream_t s = (hipStream_t)stream;
-    if (hbl::decode_fused_ok(M, K, abits, use_hadamard)) {  // a few rows: one fused kernel
-      hipError_t e = hbl::launch_decode_fused(x, (int)xt, M, K, (int)norm, norm == HBL_NORM_RMS ? gamma : nullptr,
-                                              norm_eps, abits, Wq, w_scale, N, codes, deq, y, s);
-      if (e != hipSuccess) return hip_fail(fn, e);
-      return HBL_OK;
-    }
-    hipError_t e = hbl::launch_actquant(x, (int)xt, M, K, (int)norm, norm == HBL_NORM_RMS ? gamma : nullptr,
-                                        norm_eps, abits, use_hadamard, codes, deq, s);
+    return run_forward(fn, x, xt, Wq, w_scale, M, K, N, abits, use_hadamard, norm, gamma, norm_eps, y, ws, stream);
+  } catch (...) {
+    return fail(HBL_ERR_HIP, fn, "unexpected C++ exception");
+  }
+}
+
+hbl_status hbl_forward_noalloc(const void* x, hbl_dtype xt, const uint8_t* Wq, const float* w_scale, int64_t M,
+                               int64_t K, int64_t N, int abits, int use_hadamard, hbl_norm norm, const float* gamma,
+                               float norm_eps, float* y, void* stream) {
+  static const char* fn = "hbl_forward_noalloc";
+  try {
+    HBL_TRY(check_shape(fn, M, K, N, abits));
+    HBL_TRY(check_act(fn, xt, norm, gamma, norm_eps, use_hadamard, K));
+    HBL_TRY(check_ptr(fn, Wq, "Wq", 16));
+    HBL_TRY(check_ptr(fn, w_scale, "w_scale", 4));
+    if (M == 0) return HBL_OK;
+    HBL_TRY(check_ptr(fn, x, "x", 16));
+    HBL_TRY(check_ptr(fn, y, "y", 16));
+    const size_t need = hbl_forward_workspace_bytes(M, K, abits);
+    if (need > (size_t)HBL_NOALLOC_SCRATCH_BYTES)
+      return fail(HBL_ERR_UNSUPPORTED, fn,
+                  "the codes and deq of this call need " + std::to_string(need) +
+                      " bytes, above the static scratch of HBL_NOALLOC_SCRATCH_BYTES = " +
+                      std::to_string((size_t)HBL_NOALLOC_SCRATCH_BYTES) + "; use hbl_forward with a workspace");
+    void* ws = nullptr;
+    hipError_t e = scratch_of_current_device(&ws);
     if (e != hipSuccess) return hip_fail(fn, e);
-    e = hbl::launch_gemm(codes, deq, Wq, w_scale, M, K, N, abits, nullptr, y, s);
-    if (e != hipSuccess) return hip_fail(fn, e);
-    return HBL_OK;
+    return run_forward(fn, x, xt, Wq, w_scale, M, K, N, abits, use_hadamard, norm, gamma, norm_eps, y, ws, stream);
   } catch (...) {
     return fail(HBL_ERR_HIP, fn, "unexpected C++ exception");
   }

@@ -88,7 +88,8 @@
  * Conventions for every entry point:
  *  - Every pointer argument is a device pointer (hipMalloc / torch CUDA memory) unless
  *    stated otherwise, 16-byte aligned.  The caller owns every buffer; the library never
- *    allocates device memory and keeps no mutable global state.
+ *    allocates device memory.  Its only mutable state is the static scratch array of
+ *    hbl_forward_noalloc (one per GPU) and the pointers to it.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All work is
  *    enqueued asynchronously on that stream.  Calls on different streams are independent.
  *  - Arguments are validated synchronously, before any HIP call.  An invalid argument
@@ -199,6 +200,22 @@ hbl_status hbl_quantize_activations_stat(const void* x, hbl_dtype xt, int64_t M,
 hbl_status hbl_forward_stat(const void* x, hbl_dtype xt, const uint8_t* Wq, const float* w_scale, int64_t M,
                             int64_t K, int64_t N, int abits, int use_hadamard, hbl_norm norm, const float* gamma,
                             float norm_eps, int stat, float* y, void* ws, size_t ws_bytes, void* stream);
+
+/* hbl_forward_noalloc — hbl_forward for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  The same
+ * kernels and results as hbl_forward, bit for bit, but the codes and deq of the call live in
+ * a static device array of HBL_NOALLOC_SCRATCH_BYTES that the library owns: one per GPU, on
+ * the device current at the call (the stream must belong to it), set up by the first call on
+ * that device and kept until the process ends.  The call allocates nothing.
+ *  Needs hbl_forward_workspace_bytes(M, K, abits) <= HBL_NOALLOC_SCRATCH_BYTES
+ *  (HBL_ERR_UNSUPPORTED otherwise, before any HIP call): e.g. M = 8192, K = 16384 at abits 4.
+ *  Calls on one GPU share its array: calls that overlap in time on that GPU (several streams,
+ *  or several host threads) race on it and must be ordered by the caller.  The array keeps
+ *  the last call's codes and deq; every call writes all it reads, so nothing needs clearing. */
+#define HBL_NOALLOC_SCRATCH_BYTES (80u << 20)
+hbl_status hbl_forward_noalloc(const void* x, hbl_dtype xt, const uint8_t* Wq, const float* w_scale, int64_t M,
+                               int64_t K, int64_t N, int abits, int use_hadamard, hbl_norm norm, const float* gamma,
+                               float norm_eps, float* y, void* stream);
 
 /* 1 if hbl_forward(M, K, ..., abits, use_hadamard) runs as one fused kernel, else 0.  With a
  * few token rows (use_hadamard, K = 4096 .. 16384, M <= 256 / (K / 64)), each block of the

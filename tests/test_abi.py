@@ -303,3 +303,17 @@ def test_probe_library_exports_its_entry_point():
     f.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     assert f(None, 1, 1, FAKE, S) == 1 and f(FAKE, 0, 1, FAKE, S) == 1   # rejected before any HIP call
 
+
+def test_forward_noalloc_rejects(L):
+    def call(M=16, K=256, N=256, abits=4, h=1, x=FAKE, y=FAKE, xt=B.HBL_BF16):
+        return L.hbl_forward_noalloc(x, xt, FAKE, FAKE, M, K, N, abits, h, B.HBL_NORM_RMS, None, 1e-5, y, S)
+    # the 7B Wdown batch in INT8 needs 128 MiB of codes: above the static scratch, refused
+    assert call(M=8192, K=16384, N=4096, abits=8) == B.HBL_ERR_UNSUPPORTED
+    assert "HBL_NOALLOC_SCRATCH_BYTES" in L.hbl_last_error().decode()
+    assert L.hbl_forward_workspace_bytes(8192, 16384, 4) <= 80 << 20    # ... while INT4 fits
+    assert call(M=-1) == B.HBL_ERR_INVALID_ARG
+    assert call(K=192) == B.HBL_ERR_UNSUPPORTED
+    assert call(abits=5) == B.HBL_ERR_INVALID_ARG
+    assert call(x=None) == B.HBL_ERR_INVALID_ARG
+    assert call(y=FAKE_MIS) == B.HBL_ERR_INVALID_ARG
+    assert call(M=0, x=None, y=None) == B.HBL_OK
