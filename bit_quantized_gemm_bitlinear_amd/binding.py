@@ -11,7 +11,9 @@ import os
 import threading
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libhbl.so")
+# HBL_LIBRARY names another build of the C ABI to load instead (the sanitizer test points it
+# at a host-only build of the validation layer).
+LIB_PATH = os.environ.get("HBL_LIBRARY") or os.path.join(PKG, "libhbl.so")
 
 HBL_OK, HBL_ERR_INVALID_ARG, HBL_ERR_UNSUPPORTED, HBL_ERR_WORKSPACE, HBL_ERR_HIP = range(5)
 HBL_F32, HBL_BF16 = 0, 1

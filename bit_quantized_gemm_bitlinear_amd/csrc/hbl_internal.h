@@ -25,8 +25,10 @@ hipError_t launch_actquant_mfma(const void* x, int64_t M, int64_t K, int norm, f
                                 float* deq, hipStream_t s);
 
 // The whole H-BitLinear forward for a few token rows in one kernel (k_actquant.hip): applies
-// when decode_fused_ok(M, K, abits, use_h); writes codes/deq (workspace) and y like the
-// two-kernel path, bit for bit.
+// when decode_fused_ok(M, K, abits, use_h) (plan.cpp); writes codes/deq (workspace) and y like
+// the two-kernel path, bit for bit.  One group of R = 256 / (K / 64) rows (the rows one block
+// transforms at once): with more rows the two-kernel path is faster.
+constexpr int DEC_MAX_GROUPS = 1;
 bool decode_fused_ok(int64_t M, int64_t K, int abits, int use_h);
 hipError_t launch_decode_fused(const void* x, int xt, int64_t M, int64_t K, int norm, const float* gamma, float eps,
                                int abits, const uint8_t* Wq, const float* w_scale, int64_t N, uint8_t* codes,

@@ -344,7 +344,6 @@ __global__ __launch_bounds__(block_threads<L>()) void k_actquant_pow2(
 // Every block repeats the (cheap) activation work; block 0 also writes the packed codes and
 // deq to the caller's workspace, as the two-kernel path does.  The int32 sums are exact, so
 // y equals the two-kernel path bit for bit.
-constexpr int DEC_MAX_GROUPS = 1;  // one group of R rows: more rows are faster on the two-kernel path
 
 __device__ __forceinline__ v4i dec_b_operand(uint32_t w) {
   return v4i{(int)((w << 6) & 0xC0C0C0C0u), (int)((w << 4) & 0xC0C0C0C0u), (int)((w << 2) & 0xC0C0C0C0u),
@@ -803,15 +802,6 @@ hipError_t dispatch_plain(const void* x, int64_t M, int64_t K, const float* gamm
 }
 
 }  // namespace
-
-bool decode_fused_ok(int64_t M, int64_t K, int abits, int use_h) {
-  if (!use_h || (abits != 4 && abits != 8) || M < 1) return false;
-  int L = 0;
-  while ((int64_t(1) << L) < K) ++L;
-  if (L < 12 || L > 14) return false;
-  const int64_t R = (int64_t)256 / ((int64_t(1) << L) / 64);  // rows per group (block of 256 threads)
-  return M <= DEC_MAX_GROUPS * R;
-}
 
 hipError_t launch_decode_fused(const void* x, int xt, int64_t M, int64_t K, int norm, const float* gamma, float eps,
                                int abits, const uint8_t* Wq, const float* w_scale, int64_t N, uint8_t* codes,
