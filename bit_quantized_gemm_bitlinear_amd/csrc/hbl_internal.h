@@ -53,6 +53,15 @@ GemmPlan plan_tiles(int64_t M, int64_t N, int64_t K);
 hipError_t launch_zero32(int32_t* p, int64_t n, hipStream_t s);
 hipError_t launch_dequant32(void* buf, const float* deq, const float* w_scale, int64_t M, int64_t N, hipStream_t s);
 
+// The same GEMM with its tiles loaded straight into LDS (k_gemm_dma.hip), for K a multiple of
+// the stage depth (gemm_dma_ok): tile 256 runs 256 x 256 tiles (mode 0: int32 acc, 1: dequant),
+// any other value 128 x 256 tiles; modes 2 and 3 are the fused gate/up epilogue (out: h as
+// fp32 / bf16, N = 2F interleaved rows).  Same int32 sums and output bits as launch_gemm.
+bool gemm_dma_ok(int64_t K, int abits);
+hipError_t launch_gemm_dma(int tile, int mode, const uint8_t* codes, const float* deq, const uint8_t* Wq,
+                           const float* w_scale, const float* w_scale_up, int64_t M, int64_t K, int64_t N, int abits,
+                           int32_t* acc, void* out, hipStream_t s);
+
 // Decode-regime GEMM for M <= GEMV_MAX_M token rows (k_gemv.hip); launch_gemm dispatches to it.
 constexpr int64_t GEMV_MAX_M = 64;
 hipError_t launch_gemv(const uint8_t* codes, const float* deq, const uint8_t* Wq, const float* w_scale,

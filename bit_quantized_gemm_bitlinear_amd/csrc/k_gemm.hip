@@ -417,12 +417,17 @@ hipError_t launch(const uint8_t* codes, const float* deq, const uint8_t* Wq, con
     // The fused SwiGLU epilogue runs after the whole K, so the gate/up GEMM does not split;
     // with large problems it runs 128 x 256 tiles with four waves: two blocks share a CU and
     // one block's epilogue and start-up overlap the other's MFMAs.
-    if (use_big_tiles(M, N))
+    if (use_big_tiles(M, N)) {
+      if (gemm_dma_ok(K, ABITS))
+        return launch_gemm_dma(128, MODE, codes, deq, Wq, w_scale, w_scale_up, M, K, N, ABITS, acc, out, s);
       return launch_cfg<ABITS, 128, 256, 1, 4, BKBIG, MODE>(codes, deq, Wq, w_scale, w_scale_up, M, K, N, acc, out, 1,
                                                             s);
+    }
     return launch_cfg<ABITS, 128, 128, 2, 2, 128, MODE>(codes, deq, Wq, w_scale, w_scale_up, M, K, N, acc, out, 1, s);
   } else {
     const GemmPlan p = plan_tiles(M, N, K);
+    if (p.big && p.splits == 1 && gemm_dma_ok(K, ABITS))
+      return launch_gemm_dma(256, MODE, codes, deq, Wq, w_scale, w_scale_up, M, K, N, ABITS, acc, out, s);
     if (p.big)
       return launch_cfg<ABITS, 256, 256, 2, 4, BKBIG, MODE>(codes, deq, Wq, w_scale, w_scale_up, M, K, N, acc, out,
                                                             p.splits, s);

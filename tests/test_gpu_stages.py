@@ -156,11 +156,14 @@ def test_actquant_plain_pow2_gamma(orc, L, abits):
 # tiles for the other problems above 64 rows (the decode kernel below); K = 64, 320, 384 and 576
 # leave a partial last stage (masked loads), the other K fill every stage.  The cases run 1 to 8
 # stages (INT4: 256 deep on the large tiles, otherwise 128), odd and even counts, so the
-# two-stage-ahead load pipeline is exercised at its start and end.
+# two-stage-ahead load pipeline is exercised at its start and end.  On the 256 x 256 tiles a K
+# that fills every stage (INT4: 256, 768, 2560; INT8: also 384) takes the kernel that loads its
+# tiles straight into LDS, with one to twenty stages through its three buffers; the other K take
+# the register-staged kernel.
 @pytest.mark.parametrize("M,K,N", [(1, 64, 1), (16, 256, 256), (200, 320, 136), (129, 1024, 257), (300, 2048, 520),
                                    (64, 16384, 64), (2500, 576, 2200), (2500, 1024, 2200), (2100, 64, 2060),
                                    (2100, 256, 2060), (2100, 384, 2060), (2100, 768, 2060), (3100, 64, 4000),
-                                   (3100, 384, 4000), (3100, 768, 4000)])
+                                   (3100, 256, 4000), (3100, 384, 4000), (3100, 768, 4000), (3100, 2560, 4000)])
 @pytest.mark.parametrize("abits", [4, 8])
 def test_gemm_s32_bit_exact(orc, M, K, N, abits):
     note("gemm_s32", M, K, N, abits)
@@ -215,9 +218,11 @@ def test_gemm_s32_extremes(orc):
         np.testing.assert_array_equal(acc, orc.gemm_s32(q, T))
 
 
+# 128 x 128 tiles, then 256 x 256 tiles loaded into LDS directly (K = 512) and through registers
+# (K = 1088, a partial last stage), ragged in M and N.
+@pytest.mark.parametrize("M,K,N", [(150, 1088, 200), (3100, 512, 4000), (3100, 1088, 4000)])
 @pytest.mark.parametrize("abits", [4, 8])
-def test_gemm_dequant_bit_exact(orc, abits):
-    M, K, N = 150, 1088, 200
+def test_gemm_dequant_bit_exact(orc, M, K, N, abits):
     note("gemm_dequant", M, K, N, abits)
     rng = np.random.default_rng(abits)
     Qb = 7 if abits == 4 else 127
