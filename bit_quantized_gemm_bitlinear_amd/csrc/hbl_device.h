@@ -8,6 +8,36 @@ namespace hbl {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
+typedef unsigned v4u_t __attribute__((ext_vector_type(4)));
+
+// Buffer resource over `bytes` bytes from `base` (stride 0, raw 32-bit offsets; offsets past
+// the end read zeros).
+__device__ __forceinline__ v4u_t buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  return v4u_t{(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, bytes, 0x00020000u};
+}
+
+// One 16-byte-per-lane load from global memory into LDS (buffer_load_dwordx4 ... lds): lane
+// l's bytes at rsrc base + voff + soff land at LDS byte lds_base + 16 l.  Written as inline
+// assembly: the compiler's own form makes every later LDS read wait for all loads of this kind
+// in flight (it cannot tell which LDS bytes they write), which would drain a load pipeline at
+// every step.  A kernel using it therefore waits for these loads itself (s_waitcnt vmcnt; they
+// complete in issue order), and the memory clobber keeps the compiler from moving LDS reads
+// across them.  M0 holds the LDS base (wave-uniform); one
+// wait state separates its write from the load that reads it.  M0 is a register the compiler
+// reserves: it keeps no value there across this statement in these kernels (it sets M0 only
+// for instructions they do not use), so clobbering it is safe here and its warning is silenced.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(v4u_t rsrc, uint32_t voff, uint32_t soff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff)),
+                 "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 // bf16 bit patterns live in the top half of an fp32 word; the conversion is exact.
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }

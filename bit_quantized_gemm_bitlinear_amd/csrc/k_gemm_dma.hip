@@ -29,8 +29,6 @@
 namespace hbl {
 namespace {
 
-typedef unsigned v4u_t __attribute__((ext_vector_type(4)));
-
 // Block-to-tile order as in k_gemm.hip: every XCD gets a contiguous chunk of tile ids, which
 // advance over groups of GM tile-rows.
 __device__ __forceinline__ void dma_tile_of_block(int bid, int nblk, int ntm, int ntn, int GM, int& tm, int& tn) {
@@ -45,33 +43,6 @@ __device__ __forceinline__ void dma_tile_of_block(int bid, int nblk, int ntm, in
   tm = first + r % gm;
   tn = r / gm;
 }
-
-// Buffer resource over `bytes` bytes from `base` (stride 0, raw 32-bit offsets; offsets past
-// the end read zeros).
-__device__ __forceinline__ v4u_t buffer_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t a = (uint64_t)(uintptr_t)base;
-  return v4u_t{(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, bytes, 0x00020000u};
-}
-
-// One 16-byte-per-lane load from global memory into LDS: lane l's bytes at rsrc base + voff +
-// soff land at LDS byte lds_base + 16 l.  Written as inline assembly: the compiler's own
-// form makes every later LDS read wait for all loads of this kind in flight (it cannot tell
-// which LDS bytes they write), which would drain the pipeline below at every stage.  The
-// kernel therefore waits for these loads itself (s_waitcnt vmcnt), and the memory clobber keeps
-// the compiler from moving LDS reads across them.  M0 holds the LDS base (wave-uniform); one
-// wait state separates its write from the load that reads it.  M0 is a register the compiler
-// reserves: it keeps no value there across this statement in these kernels (it sets M0 only
-// for instructions they do not use), so clobbering it is safe here and its warning is silenced.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(v4u_t rsrc, uint32_t voff, uint32_t soff, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
-               :
-               : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff)),
-                 "s"(__builtin_amdgcn_readfirstlane(lds_base))
-               : "memory", "m0");
-}
-#pragma clang diagnostic pop
 
 // Slot swizzles (16-byte units).  A rows hold 8 slots per stage: chunk c of row r sits in slot
 // c ^ ((r >> 1) & 7).  B rows hold 4 slots (INT4 stages, 256 k) or 2 (INT8, 128 k): slot s of

@@ -20,7 +20,11 @@ from tests.gpu_util import (DEQ_ULPS_MFMA, assert_close_ulps, check_codes, mfma_
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("N,K", [(1, 64), (3, 192), (257, 1024), (300, 4160), (64, 16384)])
+# Shapes: single rows, ragged row blocks (16 rows per block of the row sums), fewer chunks than
+# the row-sum ring holds (K = 64 .. 320), row sums spanning several chunks of the ordered final
+# sum (N = 16400 > 4096) with a ragged last chunk, and the 7B Wdown and gate shapes.
+@pytest.mark.parametrize("N,K", [(1, 64), (3, 192), (257, 1024), (300, 4160), (64, 16384), (16400, 320),
+                                 (4096, 16384), (16384, 4096)])
 def test_weight_quantisation_bit_exact(orc, N, K):
     note("wquant", N, K)
     W = inputs.make_weights(N, K, seed=N + K)
