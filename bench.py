@@ -597,7 +597,10 @@ def main():
     act_roofline["cold_cache"] = {"us": t_cold * 1e6, "achieved_gbs": act_bytes / t_cold / 1e9,
                                   "frac_hbm": act_bytes / t_cold / 1e9 / PEAK_HBM_GBS,
                                   "method": "512 MB read on the launch stream before each launch, median of 20"}
-    gemm_kernel = f"k_gemm<{abits}, 256, 256, 2, 4, {256 if abits == 4 else 128}, 1, {'true' if K % (256 if abits == 4 else 128) == 0 else 'false'}, false>"
+    bk = 256 if abits == 4 else 128   # stage depth of the large-tile GEMMs
+    # K a multiple of the stage depth: the kernel that loads its tiles straight into LDS
+    gemm_kernel = (f"k_gemm_dma<{abits}, 256, 256, 2, 4, 1, 3>" if K % bk == 0 else
+                   f"k_gemm<{abits}, 256, 256, 2, 4, {bk}, 1, false, false>")
     act_kernel = f"k_actquant_hm<{K.bit_length() - 1}, {abits}, 1>"
     act_roofline["kernel"] = act_kernel
     act_roofline["traffic"] = measured_traffic(act_kernel) if wl.name == "wdown_7b" else None
@@ -695,7 +698,7 @@ def main():
                      "frac": gemm_tops / PEAK_INT8_TOPS,
                      "traffic": measured_traffic(gemm_kernel) if wl.name == "wdown_7b" else None,
                      "traffic_unit": "HBM-side bytes per launch (FETCH_SIZE x2.0 + WRITE_SIZE x1.0)",
-                     "kernel": "k_gemm (ternary x INT%d, v_mfma_i32_32x32x32_i8)" % abits,
+                     "kernel": f"{gemm_kernel} (ternary x INT{abits}, v_mfma_i32_32x32x32_i8)",
                      "algorithmic": "2*M*N*K int8 ops per launch",
                      "median_us": median(t_gemm_l) * 1e6, "mean_us": t_gemm * 1e6},
         "roofline_actquant": act_roofline,
@@ -795,9 +798,10 @@ def ffn_measure(wl, steps: int, warmup: int, n_ev: int):
             "launches_per_kernel": n_ev,
             "roofline": {"bound": "mfma", "achieved": gu_tops, "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
                          "frac": gu_tops / PEAK_INT8_TOPS,
-                         "traffic": measured_traffic("k_gemm<4, 128, 256, 1, 4, 256, 3, true, false>"),
+                         "traffic": measured_traffic("k_gemm_dma<4, 128, 256, 1, 4, 3, 2>"),
                          "traffic_unit": "HBM-side bytes per launch (FETCH_SIZE x2.0 + WRITE_SIZE x1.0)",
-                         "kernel": "k_gemm fused gate/up + SwiGLU epilogue (v_mfma_i32_32x32x32_i8)",
+                         "kernel": "k_gemm_dma<4, 128, 256, 1, 4, 3, 2> (fused gate/up + SwiGLU epilogue, "
+                                   "v_mfma_i32_32x32x32_i8)",
                          "algorithmic": "2*M*(2*ffn)*hidden int8 ops per launch"}}
 
 

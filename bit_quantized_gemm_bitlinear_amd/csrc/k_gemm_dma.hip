@@ -223,47 +223,117 @@ __global__ __launch_bounds__(64 * WR * WC) __attribute__((amdgpu_waves_per_eu(2)
   // no load may still be writing this block's LDS when its waves end
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  // Epilogue: as k_gemm.hip.
+  // Epilogue.  The outputs are computed as in k_gemm.hip, then passed through LDS one 32-row
+  // MFMA tile row at a time, so that every store writes 16 contiguous bytes per lane (a wave's
+  // row segment of 64 outputs, or of 32 h values, in 16-byte pieces) instead of one element per
+  // lane scattered over two rows.  Each wave stages in a region of its own ([32][S] words; 4 S
+  // is 32 modulo the 64 banks, so the two half-waves' writes of one tile row hit different
+  // banks) inside the stage buffers, which no load writes any more once every wave has waited
+  // for its loads and passed the barrier.
+  __syncthreads();
   const int el = __lane_id();
+  const int col = el & 31, rh = 4 * (el >> 5);   // accumulator column and row offset of this lane
+  constexpr int W = MODE >= 2 ? 32 : WN;         // outputs per row of the wave's tile
+  constexpr int S = W + 8;
+  static_assert(NW * 32 * S * 4 <= NBUF * (A_BYTES + B_BYTES), "the staging regions fit the stage buffers");
+  uint32_t* stg = reinterpret_cast<uint32_t*>(lds) + wave * 32 * S;
+  const int mw = m0 + wm * WM;                   // first row of this wave's tile
   if constexpr (MODE >= 2) {
     const float ag = w_scale[0], au = w_scale_up[0];
     const int F = N / 2;
-    const int n = n0 / 2 + wn * 32 + (el & 31);
+    const int nb = n0 / 2 + wn * 32;             // first h column of the wave (F % 32 == 0)
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
+      // the accumulators of tile row i are read only from here on
+      asm volatile("" : "+a"(acc[i][0]), "+a"(acc[i][1]));
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int m = m0 + wm * WM + 32 * i + 8 * (v >> 2) + 4 * (el >> 5) + (v & 3);
-        if (m >= M || n >= F) continue;
-        const float dm = deq[m];
-        const float g = __fmul_rn(__fmul_rn((float)(acc[i][0][v] >> SHIFT), dm), ag);
-        const float u = __fmul_rn(__fmul_rn((float)(acc[i][1][v] >> SHIFT), dm), au);
-        const float hh = silu_mul(g, u);
-        if constexpr (MODE == 2) static_cast<float*>(out)[(int64_t)m * F + n] = hh;
-        else static_cast<uint16_t*>(out)[(int64_t)m * F + n] = f32_to_bf16_rne(hh);
+        const int r = 8 * (v >> 2) + rh + (v & 3);
+        const int m = mw + 32 * i + r;
+        float hh = 0.0f;
+        if (m < M) {
+          const float dm = deq[m];
+          const float g = __fmul_rn(__fmul_rn((float)(acc[i][0][v] >> SHIFT), dm), ag);
+          const float u = __fmul_rn(__fmul_rn((float)(acc[i][1][v] >> SHIFT), dm), au);
+          hh = silu_mul(g, u);
+        }
+        stg[r * S + col] = __float_as_uint(hh);
       }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if constexpr (MODE == 3) {
+        // lane: 8 consecutive h values of one row -> 16 bytes of bf16
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const int r = (el >> 2) + 16 * p, o = el & 3;
+          const int m = mw + 32 * i + r;
+          const uint4 a = *reinterpret_cast<const uint4*>(stg + r * S + 8 * o);
+          const uint4 b = *reinterpret_cast<const uint4*>(stg + r * S + 8 * o + 4);
+          if (m < M && nb < F) {
+            uint4 q;
+            q.x = f32_to_bf16_rne(__uint_as_float(a.x)) | ((uint32_t)f32_to_bf16_rne(__uint_as_float(a.y)) << 16);
+            q.y = f32_to_bf16_rne(__uint_as_float(a.z)) | ((uint32_t)f32_to_bf16_rne(__uint_as_float(a.w)) << 16);
+            q.z = f32_to_bf16_rne(__uint_as_float(b.x)) | ((uint32_t)f32_to_bf16_rne(__uint_as_float(b.y)) << 16);
+            q.w = f32_to_bf16_rne(__uint_as_float(b.z)) | ((uint32_t)f32_to_bf16_rne(__uint_as_float(b.w)) << 16);
+            *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + (int64_t)m * F + nb + 8 * o) = q;
+          }
+        }
+      } else {
+        // lane: 4 consecutive h values of one row -> 16 bytes of fp32
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const int r = (el >> 3) + 8 * p, c = el & 7;
+          const int m = mw + 32 * i + r;
+          const uint4 q = *reinterpret_cast<const uint4*>(stg + r * S + 4 * c);
+          if (m < M && nb < F) *reinterpret_cast<uint4*>(static_cast<float*>(out) + (int64_t)m * F + nb + 4 * c) = q;
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // read before the next tile row is staged
     }
     return;
   }
   float alpha = 0.0f;
   if constexpr (MODE == 1) alpha = w_scale[0];
+  uint32_t* dst = MODE == 0 ? reinterpret_cast<uint32_t*>(acc_out) : static_cast<uint32_t*>(out);
+  const int nb = n0 + wn * WN;                   // first column of this wave
+  const bool vec = (N & 3) == 0;                 // rows start 16-byte aligned
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
+    // the accumulators of tile row i are read only from here on (otherwise the compiler moves
+    // all of them to VGPRs at once and spills)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) asm volatile("" : "+a"(acc[i][j]));
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int m = m0 + wm * WM + 32 * i + 8 * (v >> 2) + 4 * (el >> 5) + (v & 3);
-      if (m >= M) continue;
+      const int r = 8 * (v >> 2) + rh + (v & 3);
+      const int m = mw + 32 * i + r;
       float dm = 0.0f;
-      if constexpr (MODE == 1) dm = deq[m];
+      if constexpr (MODE == 1) dm = m < M ? deq[m] : 0.0f;
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const int n = n0 + wn * WN + 32 * j + (el & 31);
-        if (n >= N) continue;
         const int val = acc[i][j][v] >> SHIFT;
-        if constexpr (MODE == 0) acc_out[(int64_t)m * N + n] = val;
-        else static_cast<float*>(out)[(int64_t)m * N + n] = __fmul_rn(__fmul_rn((float)val, dm), alpha);
+        stg[r * S + 32 * j + col] =
+            MODE == 0 ? (uint32_t)val : __float_as_uint(__fmul_rn(__fmul_rn((float)val, dm), alpha));
       }
     }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    // lane: 4 consecutive outputs of one row -> 16 bytes
+#pragma unroll
+    for (int p = 0; p < 32 * WN / 4 / 64; ++p) {
+      const int r = (el >> 4) + 4 * p, c = el & 15;
+      const int m = mw + 32 * i + r, n = nb + 4 * c;
+      const uint4 q = *reinterpret_cast<const uint4*>(stg + r * S + 4 * c);
+      if (m >= M || n >= N) continue;
+      uint32_t* y = dst + (int64_t)m * N + n;
+      if (vec && n + 3 < N) {
+        *reinterpret_cast<uint4*>(y) = q;
+      } else {
+        y[0] = q.x;
+        if (n + 1 < N) y[1] = q.y;
+        if (n + 2 < N) y[2] = q.z;
+        if (n + 3 < N) y[3] = q.w;
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // read before the next tile row is staged
   }
 }
 
