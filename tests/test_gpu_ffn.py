@@ -48,9 +48,11 @@ def test_interleave_layout(orc, F, K):
 
 # (M, K, F, abits): ragged rows and output columns on the 128-tile launch; 128 x 256-tile
 # launches with an even, an odd and a partial last stage count; single row and minimum F; INT8
-# with a deep K.
+# with a deep K; 128 x 256 tiles whose last column tile is a quarter full (F = 2080) and a
+# ragged last row tile.
 SHAPES = [(300, 512, 352, 4), (300, 512, 352, 8), (2048, 512, 2048, 4), (2048, 1024, 2048, 8),
-          (2048, 768, 2048, 4), (2048, 320, 2048, 8), (1, 256, 32, 4), (77, 4096, 128, 8), (513, 4096, 1056, 4)]
+          (2048, 768, 2048, 4), (2048, 320, 2048, 8), (1, 256, 32, 4), (77, 4096, 128, 8), (513, 4096, 1056, 4),
+          (2050, 512, 2080, 4), (2050, 512, 2080, 8)]
 
 
 @pytest.mark.parametrize("M,K,F,abits", SHAPES)

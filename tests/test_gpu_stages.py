@@ -167,7 +167,8 @@ def test_actquant_plain_pow2_gamma(orc, L, abits):
 @pytest.mark.parametrize("M,K,N", [(1, 64, 1), (16, 256, 256), (200, 320, 136), (129, 1024, 257), (300, 2048, 520),
                                    (64, 16384, 64), (2500, 576, 2200), (2500, 1024, 2200), (2100, 64, 2060),
                                    (2100, 256, 2060), (2100, 384, 2060), (2100, 768, 2060), (3100, 64, 4000),
-                                   (3100, 256, 4000), (3100, 384, 4000), (3100, 768, 4000), (3100, 2560, 4000)])
+                                   (3100, 256, 4000), (3100, 384, 4000), (3100, 768, 4000), (3100, 2560, 4000),
+                                   (3100, 512, 4001), (3100, 512, 4002)])
 @pytest.mark.parametrize("abits", [4, 8])
 def test_gemm_s32_bit_exact(orc, M, K, N, abits):
     note("gemm_s32", M, K, N, abits)
@@ -223,8 +224,10 @@ def test_gemm_s32_extremes(orc):
 
 
 # 128 x 128 tiles, then 256 x 256 tiles loaded into LDS directly (K = 512) and through registers
-# (K = 1088, a partial last stage), ragged in M and N.
-@pytest.mark.parametrize("M,K,N", [(150, 1088, 200), (3100, 512, 4000), (3100, 1088, 4000)])
+# (K = 1088, a partial last stage), ragged in M and N; N = 4001 and 4002 leave output rows that
+# are not 16-byte aligned (the staged epilogue then stores element by element).
+@pytest.mark.parametrize("M,K,N", [(150, 1088, 200), (3100, 512, 4000), (3100, 1088, 4000), (3100, 512, 4001),
+                                   (3100, 512, 4002)])
 @pytest.mark.parametrize("abits", [4, 8])
 def test_gemm_dequant_bit_exact(orc, M, K, N, abits):
     note("gemm_dequant", M, K, N, abits)
