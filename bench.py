@@ -913,6 +913,30 @@ def bench_decode(args, wl):
         log(f"[bench] decode M={M}: {el * 1e6:.2f} us/step, {t_graph * 1e6:.2f} from a graph ({per[M]['path']}); "
             f"separate calls: act "
             f"{t_act * 1e6:.2f} us, gemv {t_gemv * 1e6:.2f} us ({gemv_bytes / t_gemv / 1e9:.0f} GB/s)")
+    # Same-run references for launches this small, on the same stream: a device copy of one
+    # packed weight copy (16.8 MB read and written, the source rotated over the copies as the
+    # steps do) and a one-element fill (launch and completion latency alone).
+    dst = torch.empty_like(Wq0)
+    one = torch.empty(1, device=dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    for i in range(copies):
+        dst.copy_(Wqs[i])
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(steps):
+        dst.copy_(Wqs[i % copies])
+    ev[1].record(stream)
+    for i in range(steps):
+        one.fill_(1.0)
+    ev[2].record(stream)
+    torch.cuda.synchronize()
+    t_copy = ev[0].elapsed_time(ev[1]) / steps * 1e-3
+    t_fill = ev[1].elapsed_time(ev[2]) / steps * 1e-3
+    reference = {"copy_us": t_copy * 1e6, "copy_gbs": 2 * Wq0.numel() / t_copy / 1e9, "fill_us": t_fill * 1e6,
+                 "method": f"{steps} back-to-back device copies of one {Wq0.numel() / 1e6:.1f} MB weight copy "
+                           f"(source rotated over {copies}) and {steps} one-element fills, events on the launch stream"}
+    log(f"[bench] same-run references: weight-sized copy {t_copy * 1e6:.2f} us ({reference['copy_gbs']:.0f} GB/s), "
+        f"one-element fill {t_fill * 1e6:.2f} us")
     head = per[wl.M]
     out = {"metric": "H-BitLinear a4 decode tokens/s, 7B-like Wdown (weights streamed from HBM)",
            "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": args.warmup,
@@ -923,7 +947,8 @@ def bench_decode(args, wl):
            "roofline": {"bound": "hbm", "achieved": head["gemv_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                         "frac": head["gemv_gbs"] / PEAK_HBM_GBS, "traffic": None,
                         "kernel": "k_gemv (decode GEMM, v_mfma_i32_16x16x64_i8)",
-                        "algorithmic": "N*K/4 weight bytes + M*K/2 code bytes + 4*M*N output bytes per launch"}}
+                        "algorithmic": "N*K/4 weight bytes + M*K/2 code bytes + 4*M*N output bytes per launch",
+                        "same_run_reference": reference}}
     print(json.dumps(out), flush=True)
 
 

@@ -291,6 +291,184 @@ __global__ __launch_bounds__(64 * WR * WC) void k_gemm_f6f4(const uint8_t* __res
   }
 }
 
+// The same product with its tiles loaded straight into LDS (buffer_load_dwordx4 ... lds, as
+// in k_gemm_dma.hip), for 256 x 256 tiles and K a multiple of the 128-deep stage: no register
+// set stages the tiles and no ds_write stores them.  Three stage buffers of 40 KB; a stage's
+// loads are issued right after the barrier in the middle of the stage NBUF earlier and waited
+// for at the barrier in the middle of the stage before it.
+//
+// k permutation.  The matrix core takes any assignment of k to (lane half, position) as long
+// as A and B use the same, and every sum here is exact in any order.  In a stage, lane half h
+// of k-step t multiplies codes 64 h + 32 t + 0..31 of the stage: its A operands for both steps
+// are then the 48 contiguous bytes of codes 64 h .. 64 h + 63 (three 16-byte chunks, read with
+// 128-bit LDS reads; step 0 takes the first 24 bytes, step 1 the last 24) and its B operands
+// the 16-byte chunks 2 h and 2 h + 1 of the row's 64 weight bytes.
+//
+// LDS slots (16 bytes): A row r holds 6 chunks at slots 6 r + (c ^ ((r >> 3) & 1)), B row n 4
+// chunks at 4 n + (c ^ ((n >> 2) & 3)).  The 16 lanes of a 128-bit read pass (16 consecutive
+// rows, one chunk) then hit 16 different bank groups: 6 r mod 16 runs over the even values
+// twice (r and r + 8), and the XOR gives those two rows chunks of opposite parity.
+template <int MODE>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm_f6f4_dma(
+    const uint8_t* __restrict__ A, const float* __restrict__ deq, const uint8_t* __restrict__ B,
+    const float* __restrict__ w_scale, int M, int N, int K, int32_t* __restrict__ acc_out, float* __restrict__ y) {
+  constexpr int BM = 256, BN = 256, WR = 4, WC = 2, NW = WR * WC, NBUF = 3;
+  constexpr int AB = BK6 * 6 / 8, BB = BK6 / 2;   // 96 and 64 bytes per row per stage
+  constexpr int A_BYTES = BM * AB, B_BYTES = BN * BB, STAGE = A_BYTES + B_BYTES;
+  constexpr int AI = BM * 6 / 64 / NW, BI = BN * 4 / 64 / NW;   // load instructions per wave per stage
+  constexpr int WM = BM / WR, WN = BN / WC, TM = WM / 32, TN = WN / 32;
+  static_assert(AI * 64 * NW == BM * 6 && BI * 64 * NW == BN * 4, "load instructions per wave");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NBUF * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WC, wn = wave % WC;
+  const int ntm = (M + BM - 1) / BM, ntn = (N + BN - 1) / BN;
+  int tm, tn;
+  tile_order(blockIdx.x, gridDim.x, ntm, ntn, 4, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int64_t arow = (int64_t)K * 6 / 8, brow = K / 2;
+  const int KT = K / BK6;
+
+  const v4u_t rA = buffer_rsrc(A + (int64_t)m0 * arow, (uint32_t)(min(BM, M - m0) * arow));
+  const v4u_t rB = buffer_rsrc(B + (int64_t)n0 * brow, (uint32_t)(min(BN, N - n0) * brow));
+  uint32_t aoff[AI], boff[BI];   // rows past M (N) re-read the last row
+#pragma unroll
+  for (int a = 0; a < AI; ++a) {
+    const int sl = 64 * (wave * AI + a) + lane, r = sl / 6, c = (sl % 6) ^ ((r >> 3) & 1);
+    aoff[a] = (uint32_t)(min(r, M - 1 - m0) * arow + 16 * c);
+  }
+#pragma unroll
+  for (int b = 0; b < BI; ++b) {
+    const int sl = 64 * (wave * BI + b) + lane, n = sl / 4, c = (sl % 4) ^ ((n >> 2) & 3);
+    boff[b] = (uint32_t)(min(n, N - 1 - n0) * brow + 16 * c);
+  }
+  const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
+  auto load_stage = [&](int kt, int buf) __attribute__((always_inline)) {
+    const uint32_t sa = lds0 + buf * STAGE, sb = sa + A_BYTES;
+#pragma unroll
+    for (int a = 0; a < AI; ++a) dma16(rA, aoff[a], kt * AB, sa + 1024 * (wave * AI + a));
+#pragma unroll
+    for (int b = 0; b < BI; ++b) dma16(rB, boff[b], kt * BB, sb + 1024 * (wave * BI + b));
+  };
+
+  // fragment addresses within a stage buffer (rows l % 32 of the wave's tiles; half h = l / 32)
+  const int l32 = lane & 31, h = lane >> 5;
+  int afr[3], bfr[2];
+#pragma unroll
+  for (int e = 0; e < 3; ++e) afr[e] = 16 * (6 * (wm * WM + l32) + ((3 * h + e) ^ ((l32 >> 3) & 1)));
+#pragma unroll
+  for (int t = 0; t < 2; ++t) bfr[t] = A_BYTES + 16 * (4 * (wn * WN + l32) + ((2 * h + t) ^ ((l32 >> 2) & 3)));
+  // part 0 (k-step 0): A chunks 0, 1 and B chunk 0; part 1 (k-step 1): the upper half of A
+  // chunk 1 (kept from part 0), A chunk 2 and B chunk 1
+  typedef unsigned v2u_t __attribute__((ext_vector_type(2)));
+  struct F0 {
+    v4u_t a[TM][2];
+    v4u_t b[TN];
+  };
+  struct F1 {
+    v2u_t hi[TM];
+    v4u_t a[TM];
+    v4u_t b[TN];
+  };
+  auto read0 = [&](int buf, F0& f) __attribute__((always_inline)) {
+    const uint8_t* base = lds + buf * STAGE;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) f.a[i][e] = *reinterpret_cast<const v4u_t*>(base + afr[e] + 32 * 6 * 16 * i);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) f.b[j] = *reinterpret_cast<const v4u_t*>(base + bfr[0] + 32 * 4 * 16 * j);
+  };
+  auto read1 = [&](int buf, F1& f) __attribute__((always_inline)) {
+    const uint8_t* base = lds + buf * STAGE;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) f.a[i] = *reinterpret_cast<const v4u_t*>(base + afr[2] + 32 * 6 * 16 * i);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) f.b[j] = *reinterpret_cast<const v4u_t*>(base + bfr[1] + 32 * 4 * 16 * j);
+  };
+
+  v16f acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      acc[i][j] = v16f{};
+      asm volatile("" : "+a"(acc[i][j]));
+    }
+  auto mma0 = [&](const F0& f) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const v8i a = v8i{(int)f.a[i][0].x, (int)f.a[i][0].y, (int)f.a[i][0].z, (int)f.a[i][0].w,
+                        (int)f.a[i][1].x, (int)f.a[i][1].y, 0, 0};
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const v8i b = v8i{(int)f.b[j].x, (int)f.b[j].y, (int)f.b[j].z, (int)f.b[j].w, 0, 0, 0, 0};
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[i][j], 2, 4, 0, 127, 0, 127);
+      }
+    }
+  };
+  auto mma1 = [&](const F1& f) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const v8i a = v8i{(int)f.hi[i].x, (int)f.hi[i].y, (int)f.a[i].x, (int)f.a[i].y, (int)f.a[i].z, (int)f.a[i].w,
+                        0, 0};
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const v8i b = v8i{(int)f.b[j].x, (int)f.b[j].y, (int)f.b[j].z, (int)f.b[j].w, 0, 0, 0, 0};
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[i][j], 2, 4, 0, 127, 0, 127);
+      }
+    }
+  };
+
+  // Pipeline as in k_gemm_dma.hip: stage s in buffer s % NBUF, its loads issued after the
+  // middle barrier of stage s - NBUF and complete at the middle barrier of stage s - 1; past
+  // the last stage the last one is loaded again into a buffer no one reads.
+  constexpr int PER_STAGE = AI + BI;
+#pragma unroll
+  for (int st = 0; st < NBUF; ++st) load_stage(min(st, KT - 1), st);
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NBUF - 1) * PER_STAGE) : "memory");
+  __syncthreads();
+  F0 f0;
+  F1 f1;
+  read0(0, f0);
+  for (int kt = 0; kt < KT; ++kt) {
+    const int buf = kt % NBUF;
+    read1(buf, f1);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) f1.hi[i] = v2u_t{f0.a[i][1].z, f0.a[i][1].w};
+    mma0(f0);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NBUF - 2) * PER_STAGE) : "memory");
+    __syncthreads();
+    load_stage(min(kt + NBUF, KT - 1), buf);
+    read0((kt + 1) % NBUF, f0);
+    mma1(f1);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no load may still write LDS at exit
+
+  const int el = __lane_id();
+  float alpha = 0.0f;
+  if constexpr (MODE == 1) alpha = w_scale[0];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int m = m0 + wm * WM + 32 * i + 8 * (v >> 2) + 4 * (el >> 5) + (v & 3);
+      if (m >= M) continue;
+      float dm = 0.0f;
+      if constexpr (MODE == 1) dm = deq[m];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int n = n0 + wn * WN + 32 * j + (el & 31);
+        if (n >= N) continue;
+        const float a = acc[i][j][v];  // an exact integer
+        if constexpr (MODE == 0) acc_out[(int64_t)m * N + n] = (int32_t)a;
+        else y[(int64_t)m * N + n] = __fmul_rn(__fmul_rn(a, dm), alpha);
+      }
+    }
+  }
+}
+
 template <int BM, int BN, int WR, int WC, int MODE>
 hipError_t launch_cfg(const uint8_t* codes, const float* deq, const uint8_t* Wq4, const float* w_scale, int64_t M,
                       int64_t K, int64_t N, int32_t* acc, float* y, int splits, hipStream_t s) {
@@ -327,6 +505,12 @@ template <int MODE>
 hipError_t launch(const uint8_t* codes, const float* deq, const uint8_t* Wq4, const float* w_scale, int64_t M,
                   int64_t K, int64_t N, int32_t* acc, float* y, hipStream_t s) {
   const GemmPlan p = plan_tiles(M, N, K);
+  if (p.big && p.splits == 1 && K % BK6 == 0) {
+    const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+    hipLaunchKernelGGL((k_gemm_f6f4_dma<MODE>), dim3((unsigned)tiles), dim3(512), 0, s, codes, deq, Wq4, w_scale,
+                       (int)M, (int)N, (int)K, acc, y);
+    return hipGetLastError();
+  }
   if (p.big) return launch_cfg<256, 256, 4, 2, MODE>(codes, deq, Wq4, w_scale, M, K, N, acc, y, p.splits, s);
   return launch_cfg<128, 128, 2, 2, MODE>(codes, deq, Wq4, w_scale, M, K, N, acc, y, p.splits, s);
 }

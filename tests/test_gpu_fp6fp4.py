@@ -59,12 +59,14 @@ def test_actquant_fp6_plain(orc, K):
 
 # K = 64, 320, 576: partial last stage (masked loads); the others fill every 128-deep stage.
 # An odd number of stages (K = 64, 320, 576, 1152) ends on the loop's peeled last stage.
-# (3100, *, 4000) runs 256 x 256 tiles; the others 128 x 128, and (64, 16384, 64), (128, 16384,
-# 1024) and (300, 8320, 520) split K (the last with a partial last stage in its last split).
+# (3100, *, 4000/4001) runs 256 x 256 tiles, loaded straight into LDS when K fills every stage
+# (1, 3 and 10 stages through the three buffers); the others 128 x 128, and (64, 16384, 64),
+# (128, 16384, 1024) and (300, 8320, 520) split K (the last with a partial last stage in its
+# last split).
 @pytest.mark.parametrize("M,K,N", [(1, 64, 1), (200, 320, 136), (129, 1024, 257), (64, 16384, 64),
                                    (2500, 576, 2200), (2500, 1152, 2200), (2100, 64, 2060), (2100, 256, 2060),
-                                   (2100, 384, 2060), (3100, 64, 4000), (3100, 384, 4000), (128, 16384, 1024),
-                                   (300, 8320, 520)])
+                                   (2100, 384, 2060), (3100, 64, 4000), (3100, 128, 4000), (3100, 384, 4000),
+                                   (3100, 1280, 4001), (128, 16384, 1024), (300, 8320, 520)])
 def test_gemm_fp6fp4_s32(orc, M, K, N):
     note("gemm fp6fp4", M, K, N)
     rng = np.random.default_rng(M + N)
@@ -116,7 +118,11 @@ def test_forward_fp6fp4_full_size_sampled_rows(orc):
     T, alpha = orc.quantize_weights(W)
     Wq, scale = B.quantize_weights(to_dev(W))
     Wq4 = B.weights_to_fp4(Wq, wl.K)
-    y = to_host(B.forward_fp6fp4(to_dev(x), Wq4, scale, True, norm=True))
+    xd = to_dev(x)
+    y = to_host(B.forward_fp6fp4(xd, Wq4, scale, True, norm=True))
+    # every row equals the INT4 path's (whose every row the full-size forward test holds to
+    # the oracle), and sampled rows meet the oracle directly
+    np.testing.assert_array_equal(y.view(np.int32), to_host(B.forward(xd, Wq, scale, 4, True, norm=True)).view(np.int32))
     rows = np.unique(np.concatenate([np.random.default_rng(7).choice(wl.M, 30, replace=False), [0, wl.M - 1]]))
     xs = np.ascontiguousarray(x[rows])
     y_o, q_o, _, _ = orc.forward(xs, T, alpha, 4, True, norm=True, intermediates=True)
