@@ -444,27 +444,59 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
     read0((kt + 1) % NBUF, f0);
     mma1(f1);
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no load may still write LDS at exit
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no load may still write LDS
 
+  // Epilogue through LDS as in k_gemm_dma.hip: one 32-row MFMA tile row and half of the wave's
+  // columns (64) at a time, each wave in a region of its own ([32][72] words) inside the stage
+  // buffers, so that every store writes 16 contiguous bytes per lane.
+  __syncthreads();
   const int el = __lane_id();
+  const int col = el & 31, rh = 4 * (el >> 5);
+  constexpr int S = 64 + 8;   // 4 S = 32 modulo the 64 banks
+  static_assert(NW * 32 * S * 4 <= NBUF * STAGE, "the staging regions fit the stage buffers");
+  uint32_t* stg = reinterpret_cast<uint32_t*>(lds) + wave * 32 * S;
   float alpha = 0.0f;
   if constexpr (MODE == 1) alpha = w_scale[0];
+  uint32_t* dst = MODE == 0 ? reinterpret_cast<uint32_t*>(acc_out) : reinterpret_cast<uint32_t*>(y);
+  const int mw = m0 + wm * WM;
+  const bool vec = (N & 3) == 0;   // rows start 16-byte aligned
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int m = m0 + wm * WM + 32 * i + 8 * (v >> 2) + 4 * (el >> 5) + (v & 3);
-      if (m >= M) continue;
-      float dm = 0.0f;
-      if constexpr (MODE == 1) dm = deq[m];
+    for (int hj = 0; hj < TN / 2; ++hj) {
+      // the accumulators of this piece are read only from here on
+      asm volatile("" : "+a"(acc[i][2 * hj]), "+a"(acc[i][2 * hj + 1]));
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int n = n0 + wn * WN + 32 * j + (el & 31);
-        if (n >= N) continue;
-        const float a = acc[i][j][v];  // an exact integer
-        if constexpr (MODE == 0) acc_out[(int64_t)m * N + n] = (int32_t)a;
-        else y[(int64_t)m * N + n] = __fmul_rn(__fmul_rn(a, dm), alpha);
+      for (int v = 0; v < 16; ++v) {
+        const int r = 8 * (v >> 2) + rh + (v & 3);
+        const int m = mw + 32 * i + r;
+        float dm = 0.0f;
+        if constexpr (MODE == 1) dm = m < M ? deq[m] : 0.0f;
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const float a = acc[i][2 * hj + jj][v];  // an exact integer
+          stg[r * S + 32 * jj + col] =
+              MODE == 0 ? (uint32_t)(int32_t)a : __float_as_uint(__fmul_rn(__fmul_rn(a, dm), alpha));
+        }
       }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        const int r = (el >> 4) + 4 * p, c = el & 15;
+        const int m = mw + 32 * i + r, n = n0 + wn * WN + 64 * hj + 4 * c;
+        const uint4 q = *reinterpret_cast<const uint4*>(stg + r * S + 4 * c);
+        if (m >= M || n >= N) continue;
+        uint32_t* yp = dst + (int64_t)m * N + n;
+        if (vec && n + 3 < N) {
+          *reinterpret_cast<uint4*>(yp) = q;
+        } else {
+          yp[0] = q.x;
+          if (n + 1 < N) yp[1] = q.y;
+          if (n + 2 < N) yp[2] = q.z;
+          if (n + 3 < N) yp[3] = q.w;
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // read before the next piece is staged
     }
   }
 }
