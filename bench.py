@@ -533,8 +533,8 @@ def main():
                                      "gemm_fp6fp4_dequant": median(tg6_l) * 1e6},
                "roofline": {"bound": "mfma", "achieved": g6, "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s",
                             "frac": g6 / PEAK_FP4_TFLOPS,
-                            "traffic": measured_traffic("k_gemm_f6f4<256, 256, 4, 2, 1, true, false>"),
-                            "kernel": "k_gemm_f6f4<256, 256, 4, 2, 1, true, false>",
+                            "traffic": measured_traffic("k_gemm_f6f4_dma<1>"),
+                            "kernel": "k_gemm_f6f4_dma<1>",
                             "algorithmic": "2*M*N*K ops per launch"},
                "mfma_ceiling": None if not ceil6 else {
                    "tflops": ceil6, "frac_of_peak": ceil6 / PEAK_FP4_TFLOPS, "gemm_frac_of_ceiling": g6 / ceil6,
