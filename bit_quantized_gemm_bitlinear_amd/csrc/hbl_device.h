@@ -49,6 +49,17 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
 }
 
+// Two fp32 bit patterns -> two bf16 in one word (lo first), round to nearest even, by the
+// packed conversion instruction (v_cvt_pk_bf16_f32).  For every non-NaN input, denormals
+// included (the kernels run with fp32 denormals preserved), the bits are those of
+// f32_to_bf16_rne.
+__device__ __forceinline__ uint32_t bf16x2_rne(uint32_t lo, uint32_t hi) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+  const bf16x2v_t b = __builtin_convertvector(f32x2_t{__uint_as_float(lo), __uint_as_float(hi)}, bf16x2v_t);
+  return __builtin_bit_cast(uint32_t, b);
+}
+
 // e^x for the SwiGLU gate, in a few instructions: x log2(e) = n + r with n an integer and
 // |r| <= 1/2, where log2(e) is split into its fp32 value and the remainder so that r carries
 // only its own rounding; 2^r comes from v_exp_f32 and n is added to the exponent

@@ -269,11 +269,8 @@ __global__ __launch_bounds__(64 * WR * WC) __attribute__((amdgpu_waves_per_eu(2)
           const uint4 a = *reinterpret_cast<const uint4*>(stg + r * S + 8 * o);
           const uint4 b = *reinterpret_cast<const uint4*>(stg + r * S + 8 * o + 4);
           if (m < M && nb < F) {
-            uint4 q;
-            q.x = f32_to_bf16_rne(__uint_as_float(a.x)) | ((uint32_t)f32_to_bf16_rne(__uint_as_float(a.y)) << 16);
-            q.y = f32_to_bf16_rne(__uint_as_float(a.z)) | ((uint32_t)f32_to_bf16_rne(__uint_as_float(a.w)) << 16);
-            q.z = f32_to_bf16_rne(__uint_as_float(b.x)) | ((uint32_t)f32_to_bf16_rne(__uint_as_float(b.y)) << 16);
-            q.w = f32_to_bf16_rne(__uint_as_float(b.z)) | ((uint32_t)f32_to_bf16_rne(__uint_as_float(b.w)) << 16);
+            const uint4 q = make_uint4(bf16x2_rne(a.x, a.y), bf16x2_rne(a.z, a.w), bf16x2_rne(b.x, b.y),
+                                       bf16x2_rne(b.z, b.w));
             *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + (int64_t)m * F + nb + 8 * o) = q;
           }
         }
