@@ -1,5 +1,5 @@
-// actquant_mfma.h — the online Hadamard transform of bf16 activation rows with its first five
-// butterfly stages on the matrix cores, shared by the activation kernel (k_actquant_mfma.hip)
+// actquant_mfma.h — the online Hadamard transform of bf16 activation rows with five or six of
+// its butterfly stages on the matrix cores, shared by the activation kernel (k_actquant_mfma.hip)
 // and the fused decode kernel (k_actquant.hip).
 //
 // BitNet v2 write-up, section H-BitLinear模塊: the activations are normalised and then
@@ -14,7 +14,8 @@
 // index bits are transformed by fp32 butterflies in registers, around one transpose through
 // LDS.  Stage order and summation order differ from the plain in-place loop, so z agrees with
 // it up to fp32 rounding; on integer-valued rows whose transform stays below 2^24 every sum
-// is exact and z is identical.
+// is exact and z is identical.  Where the next index bit (e10) also indexes the row, its
+// butterfly is folded into the products too (hm_front).
 //
 // Layout.  A block of 4 waves transforms a slab of 16384 consecutive elements (16384 / K rows
 // of K = 2^L elements, 10 <= L <= 14); element E of the slab has index bits e0..e13 and
@@ -24,7 +25,9 @@
 //     a lane), e8 (lane half) and e9 (chunk parity).  Result lane l holds column j = l % 32,
 //     the transformed bits (e0, e1, e2, e8, e9), and 16 rows i: register bits e3, e4, e6, e7,
 //     lane bit 5 = e5, and p = (e10, e11)
-//   register stages: e3, e4, e6, e7, then e10 and e11 where they index the row
+//   e10 on the matrix cores where it indexes the row (the products then hold z's e10 bit in
+//     the place of p's)
+//   register stages: e3, e4, e6, e7, then e11 where it indexes the row
 //   LDS transpose; registers then hold runs of consecutive elements (e0, e1, e2, ...) and the
 //   bits still to transform, e5 and (for L = 13, 14) e12, e13; stages on them.
 #pragma once
@@ -202,22 +205,31 @@ struct HmStats {
   double ss;     // sum of x^2 (RMSNorm)
 };
 
-// Transforms the slab held in raw.  `after_mfma` runs once the raw registers have been read by
-// the matrix cores (the caller may reload them there).  On return v holds this thread's 64
-// values of z in the layout after the transpose and st its row's statistics.
-// Synchronisation: for L <= 12 a row lives in one wave and the wave's LDS region is its own,
-// so no block barrier is needed (LDS instructions of a wave execute in order).  For L >= 13 a
-// row spans 2 or 4 waves: one block barrier after the transpose stores, one after the partial
-// statistics are written.  Consecutive calls need no barrier between them: every wave reads
-// this slab's LDS and reduction slots before it reaches the second barrier, and writes the
-// next slab's slots only after the next call's first barrier.
-template <int L, int ABITS, int NM, typename AfterMfma>
-__device__ __forceinline__ void hm_transform(uint4 (&raw)[8], const bf16x8_t hb0, const bf16x8_t hb1,
-                                             float* __restrict__ lds, float* redf, double* redd, double* redd2,
-                                             int w, int lane, float (&v)[64], HmStats& st, AfterMfma&& after_mfma) {
-  using P = HmPost<L>;
+// Transform bits taken by the matrix cores: the five of the product with H_32, plus e10 where it
+// indexes the row (a product with H_64).
+template <int L>
+__device__ __forceinline__ constexpr int hm_mfma_bits() {
+  return L >= 11 ? 6 : 5;
+}
+
+// Front of the transform of the slab held in raw: the partial sums of squares (NM != 0) and the
+// products on the matrix cores, written to v in the matrix-core layout.  Nothing here touches
+// LDS, and raw may be reloaded as soon as this returns.
+//
+// Chunks 2p and 2p + 1 hold, for each of the 32 A rows, 32 values whose transform bits are
+// (e0, e1, e2, e8, e9): t_p = A_2p H_32[0:16] + A_2p+1 H_32[16:32] is their 32-point transform,
+// and the two bits of p are e10 and e11.  Where e10 indexes the row its 2-point butterfly is
+// folded into the products as well: the accumulator of one product is the C input of the next,
+// so t_2g + t_2g+1 and t_2g - t_2g+1 both continue from t_2g, the second with H negated (six
+// products per pair of p instead of four products and a butterfly stage).  Every product is
+// exact and the sums are fp32 sums of the matrix core, so z agrees with the butterfly order up
+// to fp32 rounding, and exactly on the integer class.
+template <int L, int NM>
+__device__ __forceinline__ void hm_front(const uint4 (&raw)[8], const bf16x8_t hb0, const bf16x8_t hb1,
+                                         float (&v)[64], float (&ssp)[4]) {
   // ---- sums of squares on the raw bf16 (squares exact; fp32 sums per pair of chunks) ----
-  float ssp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) ssp[i] = 0.0f;
   if constexpr (NM != 0) {
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
@@ -230,23 +242,54 @@ __device__ __forceinline__ void hm_transform(uint4 (&raw)[8], const bf16x8_t hb0
     }
   }
 
-  // ---- five stages on the matrix cores: D_p = A_2p H_32[0:16] + A_2p+1 H_32[16:32] ----
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    f32x16_t d = {};
-    d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, raw[2 * p]), hb0, d, 0, 0, 0);
-    d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, raw[2 * p + 1]), hb1, d, 0, 0, 0);
+  // ---- products on the matrix cores ----
+  constexpr int MB = hm_mfma_bits<L>();
+  const bf16x8_t nb0 = __builtin_bit_cast(bf16x8_t, __builtin_bit_cast(v4u_t, hb0) ^ 0x80008000u);
+  const bf16x8_t nb1 = __builtin_bit_cast(bf16x8_t, __builtin_bit_cast(v4u_t, hb1) ^ 0x80008000u);
+  // C + A_c H (H negated if neg), H's half chosen by the chunk parity e9
+  auto mma = [&](int c, bool neg, f32x16_t acc) __attribute__((always_inline)) {
+    const bf16x8_t b = (c & 1) ? (neg ? nb1 : hb1) : (neg ? nb0 : hb0);
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, raw[c]), b, acc, 0, 0, 0);
+  };
+  auto put = [&](int p, const f32x16_t& d) __attribute__((always_inline)) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) v[16 * p + r] = d[r];
+  };
+  if constexpr (MB == 5) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) put(p, mma(2 * p + 1, false, mma(2 * p, false, f32x16_t{})));
+  } else {
+    static_assert(MB == 6, "five or six bits on the matrix cores");
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const f32x16_t t = mma(4 * g + 1, false, mma(4 * g, false, f32x16_t{}));
+      put(2 * g, mma(4 * g + 3, false, mma(4 * g + 2, false, t)));
+      put(2 * g + 1, mma(4 * g + 3, true, mma(4 * g + 2, true, t)));
+    }
   }
-  after_mfma();
+}
 
-  // ---- register stages: e3, e4, e6, e7, then e10, e11 where they index the row ----
+// Back of the transform: on entry v holds the products of hm_front and ssp its partial sums of
+// squares; on return v holds this thread's 64 values of z in the layout after the transpose
+// and st its row's statistics.
+// Synchronisation: for L <= 12 a row lives in one wave and the wave's LDS region is its own,
+// so no block barrier is needed (LDS instructions of a wave execute in order).  For L >= 13 a
+// row spans 2 or 4 waves: one block barrier after the transpose stores, one after the partial
+// statistics are written.  Consecutive calls need no barrier between them: every wave reads
+// this slab's LDS and reduction slots before it reaches the second barrier, and writes the
+// next slab's slots only after the next call's first barrier.
+template <int L, int ABITS, int NM>
+__device__ __forceinline__ void hm_back(float* __restrict__ lds, float* redf, double* redd, double* redd2, int w,
+                                        int lane, float (&v)[64], const float (&ssp)[4], HmStats& st) {
+  using P = HmPost<L>;
+  constexpr int MB = hm_mfma_bits<L>();
+  // ---- register stages: e3, e4, e6, e7, then e10 (unless the matrix cores took it) and e11
+  // where they index the row ----
   hm_stage<0>(v);
   hm_stage<1>(v);
   hm_stage<2>(v);
   hm_stage<3>(v);
-  if constexpr (L >= 11) hm_stage<4>(v);
+  if constexpr (L >= 11 && MB < 6) hm_stage<4>(v);
   if constexpr (L >= 12) hm_stage<5>(v);
 
   // ---- transpose through LDS ----
@@ -351,6 +394,18 @@ __device__ __forceinline__ void hm_transform(uint4 (&raw)[8], const bf16x8_t hb0
       for (int i = 1; i < P::ROW_WAVES; ++i) st.amax = __builtin_fmaxf(st.amax, redf[w0 + i]);
     }
   }
+}
+
+// The whole transform of the slab held in raw; `after_mfma` runs once the matrix cores have
+// read raw (the caller may reload it there).
+template <int L, int ABITS, int NM, typename AfterMfma>
+__device__ __forceinline__ void hm_transform(uint4 (&raw)[8], const bf16x8_t hb0, const bf16x8_t hb1,
+                                             float* __restrict__ lds, float* redf, double* redd, double* redd2,
+                                             int w, int lane, float (&v)[64], HmStats& st, AfterMfma&& after_mfma) {
+  float ssp[4];
+  hm_front<L, NM>(raw, hb0, hb1, v, ssp);
+  after_mfma();
+  hm_back<L, ABITS, NM>(lds, redf, redd, redd2, w, lane, v, ssp, st);
 }
 
 }  // namespace

@@ -18,7 +18,7 @@ hipError_t launch_actquant(const void* x, int xt, int64_t M, int64_t K, int norm
                            float eps, int abits, int use_h, uint8_t* codes, float* deq, hipStream_t s);
 
 // bf16 rows with unit gamma and K = 2^10 .. 2^14 under the transform take the activation
-// kernel whose first five transform stages run on the matrix cores (k_actquant_mfma.hip);
+// kernel that runs five or six transform stages on the matrix cores (k_actquant_mfma.hip);
 // launch_actquant dispatches to it.  abits as launch_actquant.
 bool actquant_mfma_ok(int xt, int64_t K, const float* gamma, int norm, int use_h);
 hipError_t launch_actquant_mfma(const void* x, int64_t M, int64_t K, int norm, float eps, int abits, uint8_t* codes,

@@ -1,6 +1,6 @@
 // k_actquant_mfma.hip — the H-BitLinear activation kernel for bf16 rows (K = 2^10 .. 2^14, unit
-// gamma): load -> RMSNorm statistics -> online fast Walsh-Hadamard transform with its first
-// five stages on the matrix cores (actquant_mfma.h) -> per-token absmax (or absmean) ->
+// gamma): load -> RMSNorm statistics -> online fast Walsh-Hadamard transform with five or six
+// of its stages on the matrix cores (actquant_mfma.h) -> per-token absmax (or absmean) ->
 // INT4/INT8 codes (or INT4 codes stored as FP6) + one dequant factor per row.
 //
 // BitNet v2 write-up, section H-BitLinear模塊: LN, then the online Hadamard transform by the

@@ -42,13 +42,13 @@
  *  per-row scale, so the codes do not depend on them).
  *
  *  Summation order.  The steps above fix the result up to the order of fp32 sums.  bf16 rows
- *  with unit gamma and K = 2^10 .. 2^14 under the transform run its first five stages (index
- *  bits 0, 1, 2, 8, 9) as one product with H_32 on the bf16 matrix cores (exact products, fp32
- *  sums in the matrix core's order) and the other stages in another order than above, and take
- *  r from an fp32 sum of squares (then fp64 across lanes) and v_rsq_f32.  z then agrees with the
- *  plain loop up to fp32 rounding: a code can move by one step when z*s lies within rounding of
- *  a half-integer (at most 1e-4 of the codes; a few per million on Gaussian rows), and deq by a
- *  few ulp.  On integer-valued rows whose transform stays below 2^24 in magnitude, with no norm,
+ *  with unit gamma and K = 2^10 .. 2^14 under the transform run five or six of its stages
+ *  (index bits 0, 1, 2, 8, 9, and 10 when K >= 2^11) as products with H_32 on the bf16 matrix
+ *  cores (exact products, fp32 sums in the matrix core's order) and the other stages in another
+ *  order than above, and take r from an fp32 sum of squares (then fp64 across lanes) and
+ *  v_rsq_f32.  z then agrees with the plain loop up to fp32 rounding: a code can move by one
+ *  step when z*s lies within rounding of a half-integer (at most 1e-4 of the codes; a few per
+ *  million on Gaussian rows), and deq by a few ulp.  On integer-valued rows whose transform stays below 2^24 in magnitude, with no norm,
  *  every sum is exact and codes and deq are exactly the above.  All other inputs (fp32 rows,
  *  a gamma, other K, no transform) follow the steps above exactly, with the RMS sum of squares
  *  in fp64 in another order (deq within 2 ulp).
