@@ -40,13 +40,15 @@ hipError_t launch_gemm(const uint8_t* codes, const float* deq, const uint8_t* Wq
                        int64_t M, int64_t K, int64_t N, int abits, int32_t* acc, float* y, hipStream_t s);
 
 // Tile size and K splits of the tiled GEMMs (k_gemm.hip): 256 x 256 tiles (big) or 128 x 128,
-// and the number of blocks that share each tile's K (their int32 results added atomically).
+// and the number of blocks that share each tile's K (their int32 results added atomically);
+// below the big tiles, 64 x 128 tiles run unsplit instead where small_tiles_unsplit holds.
 constexpr int64_t CUS = 256;
 struct GemmPlan {
   bool big;
   int splits;
 };
 bool use_big_tiles(int64_t M, int64_t N);
+bool small_tiles_unsplit(int64_t M, int64_t N, int64_t K);
 GemmPlan plan_tiles(int64_t M, int64_t N, int64_t K);
 // Split-K helpers (k_gemm.hip): zero n int32, and dequantise an int32 product in place
 // (y[m, n] = fl(fl((float)acc[m, n] * deq[m]) * w_scale[0]), same bits as the epilogue).
@@ -55,8 +57,9 @@ hipError_t launch_dequant32(void* buf, const float* deq, const float* w_scale, i
 
 // The same GEMM with its tiles loaded straight into LDS (k_gemm_dma.hip), for K a multiple of
 // the stage depth (gemm_dma_ok): tile 256 runs 256 x 256 tiles (mode 0: int32 acc, 1: dequant),
-// any other value 128 x 256 tiles; modes 2 and 3 are the fused gate/up epilogue (out: h as
-// fp32 / bf16, N = 2F interleaved rows).  Same int32 sums and output bits as launch_gemm.
+// tile 64 runs 64 x 128 tiles, any other value 128 x 256 tiles; modes 2 and 3 are the fused
+// gate/up epilogue (out: h as fp32 / bf16, N = 2F interleaved rows).  Same int32 sums and
+// output bits as launch_gemm.
 bool gemm_dma_ok(int64_t K, int abits);
 hipError_t launch_gemm_dma(int tile, int mode, const uint8_t* codes, const float* deq, const uint8_t* Wq,
                            const float* w_scale, const float* w_scale_up, int64_t M, int64_t K, int64_t N, int abits,

@@ -423,6 +423,8 @@ hipError_t launch(const uint8_t* codes, const float* deq, const uint8_t* Wq, con
       return launch_cfg<ABITS, 128, 256, 1, 4, BKBIG, MODE>(codes, deq, Wq, w_scale, w_scale_up, M, K, N, acc, out, 1,
                                                             s);
     }
+    if (gemm_dma_ok(K, ABITS))
+      return launch_gemm_dma(64, MODE, codes, deq, Wq, w_scale, w_scale_up, M, K, N, ABITS, acc, out, s);
     return launch_cfg<ABITS, 128, 128, 2, 2, 128, MODE>(codes, deq, Wq, w_scale, w_scale_up, M, K, N, acc, out, 1, s);
   } else {
     const GemmPlan p = plan_tiles(M, N, K);
@@ -431,6 +433,8 @@ hipError_t launch(const uint8_t* codes, const float* deq, const uint8_t* Wq, con
     if (p.big)
       return launch_cfg<ABITS, 256, 256, 2, 4, BKBIG, MODE>(codes, deq, Wq, w_scale, w_scale_up, M, K, N, acc, out,
                                                             p.splits, s);
+    if (small_tiles_unsplit(M, N, K) && gemm_dma_ok(K, ABITS))
+      return launch_gemm_dma(64, MODE, codes, deq, Wq, w_scale, w_scale_up, M, K, N, ABITS, acc, out, s);
     return launch_cfg<ABITS, 128, 128, 2, 2, 128, MODE>(codes, deq, Wq, w_scale, w_scale_up, M, K, N, acc, out,
                                                         p.splits, s);
   }
@@ -446,6 +450,19 @@ bool use_big_tiles(int64_t M, int64_t N) {
   const double time256 = (double)((t256 + CUS - 1) / CUS) * 4.0 / 2.0;
   const double time128 = (double)((t128 + CUS - 1) / CUS) * 1.0;
   return time256 <= time128;
+}
+
+// Below the 256 x 256 tiles, the 64 x 128 tiles of the LDS-direct kernel run unsplit when there
+// are at least as many as CUs, or, for K up to 8192, a quarter of that: two or three of their
+// blocks share a CU, where a 128 x 128 tile of four waves leaves one wave per SIMD.  Measured
+// (a4 and a8, MI355X) against the 128 x 128 tiles with the K splits below: 2048^3 22 -> 16 us,
+// M = 384 / 640 / 768 (N = 2048 ... 4096, K = 4096 ... 8192) 24 -> 14 us, 22 -> 13 us and
+// 43 -> 31 us, M = 512, N = 4096, K = 16384 52 -> 39 us, M = 1000, N = 600, K = 8192 22.4 ->
+// 20.9 us; below the thresholds the splits win (M = 256, N = 4096, K = 16384: 33.5 against
+// 37.5 us; M = 128, N = 1024, K = 16384: 15 against 36 us).
+bool small_tiles_unsplit(int64_t M, int64_t N, int64_t K) {
+  const int64_t t64 = ((M + 63) / 64) * ((N + 127) / 128);
+  return t64 >= CUS || (K <= 8192 && 4 * t64 >= CUS);
 }
 
 // Tiles and K splits for the product and dequant epilogues.  When the 256 x 256 tiles fill the

@@ -156,19 +156,22 @@ def test_actquant_plain_pow2_gamma(orc, L, abits):
     _act_case(orc, xf, abits, False, norm=False)
 
 
-# Tile configurations: 256 x 256 tiles for (3100, *, 4000) (at least 192 of them), 128 x 128
+# Tile configurations: 256 x 256 tiles for (3100, *, 4000) (at least 192 of them), smaller
 # tiles for the other problems above 64 rows (the decode kernel below); K = 64, 320, 384 and 576
 # leave a partial last stage (masked loads), the other K fill every stage.  The cases run 1 to 8
 # stages (INT4: 256 deep on the large tiles, otherwise 128), odd and even counts, so the
-# two-stage-ahead load pipeline is exercised at its start and end.  On the 256 x 256 tiles a K
-# that fills every stage (INT4: 256, 768, 2560; INT8: also 384) takes the kernel that loads its
-# tiles straight into LDS, with one to twenty stages through its three buffers; the other K take
-# the register-staged kernel.
+# two-stage-ahead load pipeline is exercised at its start and end.  A K that fills every stage
+# (INT4: 256, 512, 768, 1024, 2048, 2560, 8192; INT8: also 384) takes the kernel that loads its
+# tiles straight into LDS: 256 x 256 tiles with one to twenty stages through its three buffers,
+# or 64 x 128 tiles for the (2500, *, 2200), (2100, *, 206x), 2048^2 and (1000, 8192, 600)
+# problems (unaligned rows at N = 2061; the last needs no K split on these tiles); the other K
+# take the register-staged kernel (128 x 128 tiles below 192 large tiles).
 @pytest.mark.parametrize("M,K,N", [(1, 64, 1), (16, 256, 256), (200, 320, 136), (129, 1024, 257), (300, 2048, 520),
                                    (64, 16384, 64), (2500, 576, 2200), (2500, 1024, 2200), (2100, 64, 2060),
                                    (2100, 256, 2060), (2100, 384, 2060), (2100, 768, 2060), (3100, 64, 4000),
                                    (3100, 256, 4000), (3100, 384, 4000), (3100, 768, 4000), (3100, 2560, 4000),
-                                   (3100, 512, 4001), (3100, 512, 4002)])
+                                   (3100, 512, 4001), (3100, 512, 4002), (2100, 512, 2061), (512, 2048, 2048),
+                                   (1000, 8192, 600)])
 @pytest.mark.parametrize("abits", [4, 8])
 def test_gemm_s32_bit_exact(orc, M, K, N, abits):
     note("gemm_s32", M, K, N, abits)
@@ -181,9 +184,10 @@ def test_gemm_s32_bit_exact(orc, M, K, N, abits):
 
 
 # Mid-size problems whose tiles alone leave CUs idle split K over several blocks that add
-# their int32 results atomically: 8 splits of 16 stages, 4 splits of 16, and 8 splits of 9
-# stages whose last has only 2, the second of them partial (K = 8320).
-@pytest.mark.parametrize("M,K,N", [(128, 16384, 1024), (1000, 8192, 600), (300, 8320, 520)])
+# their int32 results atomically: 8 splits of 16 stages, 4 splits of 17 stages whose last has
+# 14, and 8 splits of 9 stages whose last has only 2, the second and third with a partial last
+# stage (K = 8320).
+@pytest.mark.parametrize("M,K,N", [(128, 16384, 1024), (1000, 8320, 600), (300, 8320, 520)])
 @pytest.mark.parametrize("abits", [4, 8])
 def test_gemm_s32_split_k(orc, M, K, N, abits):
     note("gemm_s32 split K", M, K, N, abits)
@@ -224,10 +228,11 @@ def test_gemm_s32_extremes(orc):
 
 
 # 128 x 128 tiles, then 256 x 256 tiles loaded into LDS directly (K = 512) and through registers
-# (K = 1088, a partial last stage), ragged in M and N; N = 4001 and 4002 leave output rows that
-# are not 16-byte aligned (the staged epilogue then stores element by element).
+# (K = 1088, a partial last stage), and 64 x 128 tiles loaded into LDS directly (2100 x 2062),
+# ragged in M and N; N = 4001, 4002 and 2062 leave output rows that are not 16-byte aligned (the
+# staged epilogue then stores element by element).
 @pytest.mark.parametrize("M,K,N", [(150, 1088, 200), (3100, 512, 4000), (3100, 1088, 4000), (3100, 512, 4001),
-                                   (3100, 512, 4002)])
+                                   (3100, 512, 4002), (2100, 512, 2062)])
 @pytest.mark.parametrize("abits", [4, 8])
 def test_gemm_dequant_bit_exact(orc, M, K, N, abits):
     note("gemm_dequant", M, K, N, abits)
