@@ -23,14 +23,16 @@ namespace {
 
 // Row sums.  A block owns RS_ROWS = 16 rows and has two waves.  The chain of each row (one
 // fp64 addition per weight, in ascending k) runs in lanes 0..15 of the second wave, which does
-// nothing else: its additions wait only for one another.  The first wave feeds it.  It streams the rows through a ring of NB float chunks (64 weights per row, 4 KB)
-// in LDS with 16-byte-per-lane loads straight into LDS, issued NB chunks ahead (lanes 16 r' + p
-// of load i fetch row 4 i + r', float4 p ^ row, so float4 j of row r sits at slot j ^ r), and
-// converts each chunk to fp64 |w| into a ring of RS_DB double chunks, two chunks ahead of the
-// chain (double pair m of row r at 16-byte slot m ^ r: the chain lanes' reads of pair m of
-// their rows hit 16 different bank groups).  (fp32 -> fp64 conversion issues at a quarter of the addition rate, so a wave doing
-// both per element would be held up by the conversions.)  One barrier per chunk.  NB = 8 when
-// every block is resident at once anyway; with many rows NB = 4 lets four blocks share a CU.
+// nothing else: its additions wait only for one another.  The first wave feeds it.  It streams
+// the rows through a ring of NB float chunks (64 weights per row, 4 KB) in LDS with
+// 16-byte-per-lane loads straight into LDS, issued NB chunks ahead (lanes 16 r' + p of load i
+// fetch row 4 i + r', float4 p ^ row, so float4 j of row r sits at slot j ^ r), and converts
+// each chunk to fp64 |w| into a ring of RS_DB double chunks, two chunks ahead of the chain
+// (double pair m of row r at 16-byte slot m ^ r: the chain lanes' reads of pair m of their
+// rows hit 16 different bank groups).  (fp32 -> fp64 conversion issues at a quarter of the
+// addition rate, so a wave doing both per element would be held up by the conversions.)  One
+// barrier per chunk.  NB = 8 when every block is resident at once anyway; with many rows
+// NB = 4 lets four blocks share a CU.
 constexpr int RS_ROWS = 16, RS_CH = 64, RS_DB = 3;
 constexpr int RS_CHUNK_BYTES = RS_ROWS * RS_CH * 4;    // 4096: one float chunk
 constexpr int RS_DROW = RS_CH * 8;                     // bytes per row of a double chunk
@@ -100,44 +102,59 @@ __global__ __launch_bounds__(128) void wq_rowsum(const float* __restrict__ W, in
     // ---- chain ----  Double chunk c is complete from the barrier after its conversion on;
     // its slot is rewritten only after the barrier that follows the last addition from it.
     // The reads run one group of 16 weights ahead of the additions, across chunk boundaries.
+    // The loop is unrolled over the RS_DB slots, so a read is a per-lane offset (computed once)
+    // plus a constant: the chain's wave issues nothing but reads, waits and additions.
     const int r = lane & 15;
     constexpr int G = 16, NG = RS_CH / G;   // weights per group, groups per chunk
-    auto read_group = [&](int c, int g, double (&d)[G]) __attribute__((always_inline)) {
-      const uint8_t* src = dring + (c % RS_DB) * RS_DCHUNK + r * RS_DROW;
+    uint32_t off[RS_CH / 2];                // double pair j of this lane's row, in a slot
+#pragma unroll
+    for (int j = 0; j < RS_CH / 2; ++j) off[j] = (uint32_t)(r * RS_DROW + 16 * (j ^ r));
+    auto read_group = [&](int slot, int g, double (&d)[G]) __attribute__((always_inline)) {
+      const uint8_t* src = dring + slot * RS_DCHUNK;
 #pragma unroll
       for (int i = 0; i < G / 2; ++i) {
-        const double2 v = *reinterpret_cast<const double2*>(src + 16 * ((G / 2 * g + i) ^ r));
+        const double2 v = *reinterpret_cast<const double2*>(src + off[G / 2 * g + i]);
         d[2 * i] = v.x;
         d[2 * i + 1] = v.y;
       }
     };
     double s = 0.0;
     double ga[G], gb[G];
-    __syncthreads();   // double chunk 0 is ready
-    if (lane < RS_ROWS) read_group(0, 0, ga);
-    __syncthreads();   // double chunk 1 is ready
-    for (int c = 0; c < C; ++c) {
+    // the additions of chunk c from slot `slot`, then the barrier after them
+    auto chunk = [&](int slot) __attribute__((always_inline)) {
       if (lane < RS_ROWS) {
 #pragma unroll
         for (int g = 0; g < NG; g += 2) {
           // (each empty statement keeps the additions after the reads issued before it)
-          read_group(c, g + 1, gb);
+          read_group(slot, g + 1, gb);
           asm volatile("" : "+v"(s)::"memory");
 #pragma unroll
           for (int u = 0; u < G; ++u) s += ga[u];
-          // the last group's successor is group 0 of chunk c + 1 (past the last chunk: a stale
-          // slot, never added)
-          if (g + 2 < NG) read_group(c, g + 2, ga);
-          else read_group(c + 1, 0, ga);
+          // the last group's successor is group 0 of the next chunk (past the last chunk: a
+          // stale slot, never added)
+          if (g + 2 < NG) read_group(slot, g + 2, ga);
+          else read_group((slot + 1) % RS_DB, 0, ga);
           asm volatile("" : "+v"(s)::"memory");
 #pragma unroll
           for (int u = 0; u < G; ++u) s += gb[u];
         }
       }
-      // every addition from chunk c is done, so its reads have returned
+      // every addition from this chunk is done, so its reads have returned
       asm volatile("" : "+v"(s)::"memory");
       __syncthreads();
+    };
+    static_assert(RS_DB == 3, "the loop below is unrolled over three slots");
+    __syncthreads();   // double chunk 0 is ready
+    if (lane < RS_ROWS) read_group(0, 0, ga);
+    __syncthreads();   // double chunk 1 is ready
+    int c = 0;
+    for (; c + 3 <= C; c += 3) {
+      chunk(0);
+      chunk(1);
+      chunk(2);
     }
+    if (c < C) chunk(0);
+    if (c + 1 < C) chunk(1);
     if (lane < rows) rowsum[n0 + lane] = s;
   }
 }
