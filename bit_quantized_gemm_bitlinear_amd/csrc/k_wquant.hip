@@ -27,27 +27,30 @@ namespace {
 // the rows through a ring of NB float chunks (64 weights per row, 4 KB) in LDS with
 // 16-byte-per-lane loads straight into LDS, issued NB chunks ahead (lanes 16 r' + p of load i
 // fetch row 4 i + r', float4 p ^ row, so float4 j of row r sits at slot j ^ r), and converts
-// each chunk to fp64 |w| into a ring of RS_DB double chunks, two chunks ahead of the chain
+// each chunk to fp64 |w| into a ring of double chunks, ahead of the chain
 // (double pair m of row r at 16-byte slot m ^ r: the chain lanes' reads of pair m of their
 // rows hit 16 different bank groups).  (fp32 -> fp64 conversion issues at a quarter of the
 // addition rate, so a wave doing both per element would be held up by the conversions.)  One
-// barrier per chunk.  NB = 8 when every block is resident at once anyway; with many rows
-// NB = 4 lets four blocks share a CU.
-constexpr int RS_ROWS = 16, RS_CH = 64, RS_DB = 3;
+// barrier per CPB chunks (3 CPB double slots: the feeder works CPB + 1 to 2 CPB chunks ahead
+// of the chain).  NB = 8 and CPB = 2 (80 KB, two blocks per CU) when every block is resident at
+// once anyway; with many rows NB = 4 and CPB = 1 (40 KB) let four blocks share a CU.
+constexpr int RS_ROWS = 16, RS_CH = 64;
 constexpr int RS_CHUNK_BYTES = RS_ROWS * RS_CH * 4;    // 4096: one float chunk
 constexpr int RS_DROW = RS_CH * 8;                     // bytes per row of a double chunk
 constexpr int RS_DCHUNK = RS_ROWS * RS_DROW;           // 8192
 
-template <int NB>
+template <int NB, int CPB>
 __global__ __launch_bounds__(128) void wq_rowsum(const float* __restrict__ W, int64_t N, int64_t K,
                                                  double* __restrict__ rowsum) {
+  constexpr int DB = 3 * CPB;   // double slots
   __shared__ __attribute__((aligned(1024))) uint8_t ring[NB * RS_CHUNK_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t dring[RS_DB * RS_DCHUNK];
+  __shared__ __attribute__((aligned(16))) uint8_t dring[DB * RS_DCHUNK];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t n0 = (int64_t)blockIdx.x * RS_ROWS;
   const int rows = (int)min((int64_t)RS_ROWS, N - n0);
   const int C = (int)(K / RS_CH);   // chunks (K % 64 == 0)
+  const int P = (C + CPB - 1) / CPB;   // barrier intervals: chunks CPB p .. CPB p + CPB - 1
 
   if (wave == 0) {
     // ---- feeder ----
@@ -77,7 +80,7 @@ __global__ __launch_bounds__(128) void wq_rowsum(const float* __restrict__ W, in
       float4 f[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) f[i] = *reinterpret_cast<const float4*>(src + 16 * ((4 * q + i) ^ r));
-      uint8_t* dst = dring + (c % RS_DB) * RS_DCHUNK + r * RS_DROW;
+      uint8_t* dst = dring + (c % DB) * RS_DCHUNK + r * RS_DROW;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = 8 * q + 2 * i;   // double pairs m, m + 1 of the row
@@ -89,12 +92,15 @@ __global__ __launch_bounds__(128) void wq_rowsum(const float* __restrict__ W, in
     };
 #pragma unroll
     for (int c = 0; c < NB; ++c) load_chunk(c);
-    convert(0);
+    // chunks 0 .. CPB before the first barrier; in interval p, chunks CPB p + CPB + 1 ..
+    // CPB p + 2 CPB, whose slots held chunks of interval p - 2 and the first of p - 1
+    for (int c = 0; c <= CPB; ++c)
+      if (c < C) convert(c);
     __syncthreads();
-    convert(1);
-    __syncthreads();
-    for (int c = 0; c < C; ++c) {
-      if (c + 2 < C) convert(c + 2);
+    for (int p = 0; p < P; ++p) {
+#pragma unroll
+      for (int k = 1; k <= CPB; ++k)
+        if (CPB * p + CPB + k < C) convert(CPB * p + CPB + k);
       __syncthreads();
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no load may still write LDS at exit
@@ -102,7 +108,7 @@ __global__ __launch_bounds__(128) void wq_rowsum(const float* __restrict__ W, in
     // ---- chain ----  Double chunk c is complete from the barrier after its conversion on;
     // its slot is rewritten only after the barrier that follows the last addition from it.
     // The reads run one group of 16 weights ahead of the additions, across chunk boundaries.
-    // The loop is unrolled over the RS_DB slots, so a read is a per-lane offset (computed once)
+    // The loop is unrolled over the DB slots, so a read is a per-lane offset (computed once)
     // plus a constant: the chain's wave issues nothing but reads, waits and additions.
     const int r = lane & 15;
     constexpr int G = 16, NG = RS_CH / G;   // weights per group, groups per chunk
@@ -120,7 +126,7 @@ __global__ __launch_bounds__(128) void wq_rowsum(const float* __restrict__ W, in
     };
     double s = 0.0;
     double ga[G], gb[G];
-    // the additions of chunk c from slot `slot`, then the barrier after them
+    // the additions of the chunk in slot `slot`
     auto chunk = [&](int slot) __attribute__((always_inline)) {
       if (lane < RS_ROWS) {
 #pragma unroll
@@ -133,28 +139,32 @@ __global__ __launch_bounds__(128) void wq_rowsum(const float* __restrict__ W, in
           // the last group's successor is group 0 of the next chunk (past the last chunk: a
           // stale slot, never added)
           if (g + 2 < NG) read_group(slot, g + 2, ga);
-          else read_group((slot + 1) % RS_DB, 0, ga);
+          else read_group((slot + 1) % DB, 0, ga);
           asm volatile("" : "+v"(s)::"memory");
 #pragma unroll
           for (int u = 0; u < G; ++u) s += gb[u];
         }
       }
-      // every addition from this chunk is done, so its reads have returned
+    };
+    // interval p, its first chunk in slot `slot0`, then the barrier after it (every addition
+    // from its chunks is done, so their reads have returned)
+    auto interval = [&](int p, int slot0) __attribute__((always_inline)) {
+#pragma unroll
+      for (int k = 0; k < CPB; ++k)
+        if (CPB * p + k < C) chunk(slot0 + k);
       asm volatile("" : "+v"(s)::"memory");
       __syncthreads();
     };
-    static_assert(RS_DB == 3, "the loop below is unrolled over three slots");
-    __syncthreads();   // double chunk 0 is ready
+    __syncthreads();   // double chunks 0 .. CPB are ready
     if (lane < RS_ROWS) read_group(0, 0, ga);
-    __syncthreads();   // double chunk 1 is ready
-    int c = 0;
-    for (; c + 3 <= C; c += 3) {
-      chunk(0);
-      chunk(1);
-      chunk(2);
+    int p = 0;
+    for (; p + 3 <= P; p += 3) {
+      interval(p, 0);
+      interval(p + 1, CPB);
+      interval(p + 2, 2 * CPB);
     }
-    if (c < C) chunk(0);
-    if (c + 1 < C) chunk(1);
+    if (p < P) interval(p, 0);
+    if (p + 1 < P) interval(p + 1, CPB);
     if (lane < rows) rowsum[n0 + lane] = s;
   }
 }
@@ -246,9 +256,9 @@ hipError_t launch_wquant(const float* W, int64_t N, int64_t K, uint8_t* Wq, floa
                          hipStream_t s) {
   const int64_t rblocks = (N + RS_ROWS - 1) / RS_ROWS;
   if (rblocks > 2 * CUS)
-    hipLaunchKernelGGL(wq_rowsum<4>, dim3((unsigned)rblocks), dim3(128), 0, s, W, N, K, ws);
+    hipLaunchKernelGGL((wq_rowsum<4, 1>), dim3((unsigned)rblocks), dim3(128), 0, s, W, N, K, ws);
   else
-    hipLaunchKernelGGL(wq_rowsum<8>, dim3((unsigned)rblocks), dim3(128), 0, s, W, N, K, ws);
+    hipLaunchKernelGGL((wq_rowsum<8, 2>), dim3((unsigned)rblocks), dim3(128), 0, s, W, N, K, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(wq_scale, dim3(1), dim3(256), 0, s, ws, N, K, w_scale);
