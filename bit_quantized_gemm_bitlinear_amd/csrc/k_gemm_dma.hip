@@ -350,10 +350,11 @@ hipError_t launch_dma(int tile, const uint8_t* codes, const float* deq, const ui
                       hipStream_t s) {
   if (tile == 256) return launch_dma_cfg<ABITS, 256, 256, 2, 4, MODE, 3>(codes, deq, Wq, w_scale, w_scale_up, M, K, N,
                                                                          acc, out, s);
-  // 64 x 128 tiles of four waves (32 x 64 each), 48 KB (INT8: 36 KB) of stage buffers and 136
-  // registers: two or three blocks share a CU, so problems of a few hundred tiles still put two
-  // waves on every SIMD
-  if (tile == 64) return launch_dma_cfg<ABITS, 64, 128, 2, 2, MODE, 3>(codes, deq, Wq, w_scale, w_scale_up, M, K, N,
+  // 64 x 128 tiles of four waves (32 x 64 each), four stage buffers (loads three stages ahead:
+  // these problems have few stages, so the first loads' latency weighs), 64 KB (INT8: 48 KB) of
+  // LDS and 136 registers: two (INT8: three) blocks share a CU, so problems of a few hundred
+  // tiles still put two waves on every SIMD
+  if (tile == 64) return launch_dma_cfg<ABITS, 64, 128, 2, 2, MODE, 4>(codes, deq, Wq, w_scale, w_scale_up, M, K, N,
                                                                       acc, out, s);
   return launch_dma_cfg<ABITS, 128, 256, 1, 4, MODE, 2>(codes, deq, Wq, w_scale, w_scale_up, M, K, N, acc, out, s);
 }
