@@ -455,7 +455,8 @@ bool use_big_tiles(int64_t M, int64_t N) {
 // Below the 256 x 256 tiles, the 64 x 128 tiles of the LDS-direct kernel run unsplit when there
 // are at least as many as CUs, or, for K up to 8192, a quarter of that: two or three of their
 // blocks share a CU, where a 128 x 128 tile of four waves leaves one wave per SIMD.  Measured
-// (a4 and a8, MI355X) against the 128 x 128 tiles with the K splits below: 2048^3 22 -> 16 us,
+// (a4 and a8, MI355X, with three stage buffers on the small tiles; four are a little faster
+// again) against the 128 x 128 tiles with the K splits below: 2048^3 22 -> 16 us,
 // M = 384 / 640 / 768 (N = 2048 ... 4096, K = 4096 ... 8192) 24 -> 14 us, 22 -> 13 us and
 // 43 -> 31 us, M = 512, N = 4096, K = 16384 52 -> 39 us, M = 1000, N = 600, K = 8192 22.4 ->
 // 20.9 us; below the thresholds the splits win (M = 256, N = 4096, K = 16384: 33.5 against
