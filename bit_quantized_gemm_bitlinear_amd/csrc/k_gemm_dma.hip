@@ -77,8 +77,14 @@ __global__ __launch_bounds__(64 * WR * WC) __attribute__((amdgpu_waves_per_eu(2)
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WC, wn = wave % WC;
   const int ntm = (M + BM - 1) / BM, ntn = (N + BN - 1) / BN;
+  // Tile-rows per group: the 32 CUs of an XCD work on GM tile-rows at once, and the operand
+  // slices those tiles stream should fit its 4 MB L2.  256 x 256 tiles (one per CU): 4 rows x 8
+  // columns.  128 x 256 tiles (the gate/up GEMM, two per CU): 8 rows x 8 columns, 2 MB of codes
+  // and 2 MB of weights over K = 4096, where 4 x 16 streamed 5 MB (632 -> 520 MB fetched from
+  // beyond L2 per 7B gate/up launch).
+  constexpr int GM = BM == 128 ? 8 : 4;
   int tm, tn;
-  dma_tile_of_block(blockIdx.x, gridDim.x, ntm, ntn, 4, tm, tn);
+  dma_tile_of_block(blockIdx.x, gridDim.x, ntm, ntn, GM, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int64_t arow = (int64_t)K * ABITS / 8;
   const int64_t brow = K / 4;
